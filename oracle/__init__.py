@@ -1,0 +1,22 @@
+"""CPU oracle for the Q4_0 weight-only linear layer (test infrastructure only).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg import this
+package.  It shares no code with the HIP library or its binding.
+"""
+
+from .q4_0_oracle import (  # noqa: F401
+    BLOCK_BYTES,
+    QK,
+    bf16_bits_to_f64,
+    dequantize,
+    error_bound,
+    gguf_bytes,
+    gguf_decode,
+    gguf_encode,
+    linear,
+    linear_rows,
+    pack,
+    packed_bytes,
+    padded_dims,
+    quantize,
+)

@@ -1,0 +1,229 @@
+"""Plain CPU oracle for the Q4_0 weight-only linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU
+baseline leg of the benchmark may import this module.  The product path (the
+HIP library and its Python binding) never calls it and shares no code with it.
+
+What the oracle computes, and where each step comes from:
+
+* The weight format is GGUF Q4_0, the format named for the quantized Voxtral
+  checkpoints ("Voxtral Mini 4B Realtime (Rust) -- Shannon-Prime Fork",
+  section "RTF Benchmark Results": model "Voxtral Mini 4B Q4_0 GGUF"; and the
+  hakusoku summary page "Voxtral Mini 4B Realtime 概要", section "推論パス",
+  "GGUF Q4_0").  A block holds 32 consecutive weights of one output row: an
+  fp16 scale d followed by 16 bytes of 4-bit codes q, and a weight decodes as
+  w = (q - 8) * d.  Byte j of the 16 holds element j in its low nibble and
+  element j + 16 in its high nibble.  18 bytes per 32 weights is what the
+  hakusoku page's section "線形演算・埋め込み" implies: the 131072 x 3072 Q4
+  embedding is 216 MB there (131072 * 3072 / 32 * 18 B = 216 MiB).
+* The layer is y = x W^T with W stored [N, K] (output rows, input columns)
+  and x given as bf16, y returned in fp64 here (fp32 on the device).  The
+  pages fuse dequantization into the matmul ("線形演算": a custom WGSL shader
+  fusing dequant + matmul); fusion changes no arithmetic, so the oracle is the
+  unfused definition: dequantize, then multiply.
+* Quantizer (host, off the timed path; the pages' counterpart is the offline
+  script scripts/quantize_tts_gguf.py in "Model Preparation"): per block the
+  signed element of largest magnitude (lowest index on ties) is amax,
+  d = fp16(amax / -8), q = clamp(rint(w / d) + 8, 0, 15) with the division in
+  fp32 and rint rounding half to even; a block whose fp16 d is zero stores
+  d = +0 and q = 8.
+* The packed device layout (the "CDNA4 tiled layout") is restated here from
+  its definition in include/q4_0.h so the device repack can be checked byte
+  for byte.  It is a permutation of the GGUF bytes, plus zero padding.
+
+Everything here is NumPy on the CPU, in fp64 where it computes values.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+QK = 32              # weights per Q4_0 block
+BLOCK_BYTES = 18     # 2 bytes fp16 scale + 16 bytes of nibbles
+
+# Device layout granularity (include/q4_0.h, "Packed layout").
+TILE_ROWS = 16       # output rows per super-tile
+TILE_BLOCKS = 4      # Q4_0 blocks (of 32 k) per super-tile
+TILE_K = TILE_BLOCKS * QK          # 128
+TILE_NIB_BYTES = 1024              # 16 rows * 4 blocks * 16 B
+TILE_SCALE_BYTES = 128             # 16 rows * 4 blocks * 2 B
+
+
+# ----------------------------------------------------------------- bf16 input
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to fp64 exactly.
+
+    A bf16 value is the top half of an fp32 value, so shifting the 16 bits
+    into the high half of a 32-bit word gives the fp32 value with the same
+    number; fp32 -> fp64 is exact.
+    """
+    u16 = np.ascontiguousarray(bits).view(np.uint16)
+    u32 = u16.astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------ GGUF Q4_0 block
+def gguf_decode(blocks: np.ndarray, n: int, k: int):
+    """Split GGUF Q4_0 bytes [n, k/32, 18] into (d fp16 [n, k/32], q uint8 [n, k]).
+
+    Bytes 0-1 of a block are d, little-endian fp16.  Of the 16 code bytes,
+    byte j carries q[j] in bits 0-3 and q[j+16] in bits 4-7.
+    """
+    if k % QK:
+        raise ValueError("K must be a multiple of 32")
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(n, k // QK, BLOCK_BYTES)
+    d = b[:, :, 0:2].copy().view("<f2").reshape(n, k // QK)
+    codes = b[:, :, 2:18]
+    q = np.empty((n, k // QK, QK), dtype=np.uint8)
+    q[:, :, 0:16] = codes & 0x0F
+    q[:, :, 16:32] = codes >> 4
+    return d, q.reshape(n, k)
+
+
+def gguf_encode(d: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Inverse of gguf_decode: (d fp16 [n, k/32], q [n, k] in 0..15) -> bytes."""
+    n, k = q.shape
+    if k % QK:
+        raise ValueError("K must be a multiple of 32")
+    if q.max(initial=0) > 15:
+        raise ValueError("codes must be 4-bit")
+    qb = q.astype(np.uint8).reshape(n, k // QK, QK)
+    out = np.empty((n, k // QK, BLOCK_BYTES), dtype=np.uint8)
+    out[:, :, 0:2] = np.ascontiguousarray(d, dtype="<f2").reshape(n, k // QK, 1).view(np.uint8)
+    out[:, :, 2:18] = qb[:, :, 0:16] | (qb[:, :, 16:32] << 4)
+    return out
+
+
+def gguf_bytes(n: int, k: int) -> int:
+    """Size of an [n, k] Q4_0 matrix in GGUF form."""
+    return n * (k // QK) * BLOCK_BYTES
+
+
+# ------------------------------------------------------------------- dequant
+def dequantize(blocks: np.ndarray, n: int, k: int) -> np.ndarray:
+    """w = (q - 8) * d, evaluated in fp32 as the device does.
+
+    The product is exact in fp32: |q - 8| <= 8 needs 4 significant bits and an
+    fp16 d at most 11, so (q - 8) * d needs at most 15 of fp32's 24.
+    """
+    d, q = gguf_decode(blocks, n, k)
+    qf = q.astype(np.float32) - np.float32(8)
+    df = np.repeat(d.astype(np.float32), QK, axis=1)
+    return qf * df
+
+
+# --------------------------------------------------------------------- linear
+def linear(x_bits: np.ndarray, blocks: np.ndarray, n: int, k: int,
+           chunk_rows: int = 8192) -> np.ndarray:
+    """y[m, j] = sum_k x[m, k] * w[j, k] in fp64; x given as bf16 bits [m, k].
+
+    Every product of a bf16 x and a dequantized weight is exact in fp64; only
+    the summation rounds.  Rows of W are processed in chunks to bound memory.
+    """
+    x = bf16_bits_to_f64(x_bits).reshape(-1, k)
+    m = x.shape[0]
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(n, k // QK, BLOCK_BYTES)
+    y = np.empty((m, n), dtype=np.float64)
+    for r0 in range(0, n, chunk_rows):
+        r1 = min(n, r0 + chunk_rows)
+        w = dequantize(b[r0:r1], r1 - r0, k).astype(np.float64)
+        y[:, r0:r1] = x @ w.T
+    return y
+
+
+def error_bound(x_bits: np.ndarray, blocks: np.ndarray, n: int, k: int,
+                chunk_rows: int = 8192) -> np.ndarray:
+    """Per-output tolerance 1e-3 * sum_k |x_k * w_k| + 1e-6 (fp64)."""
+    x = np.abs(bf16_bits_to_f64(x_bits).reshape(-1, k))
+    m = x.shape[0]
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(n, k // QK, BLOCK_BYTES)
+    out = np.empty((m, n), dtype=np.float64)
+    for r0 in range(0, n, chunk_rows):
+        r1 = min(n, r0 + chunk_rows)
+        w = np.abs(dequantize(b[r0:r1], r1 - r0, k).astype(np.float64))
+        out[:, r0:r1] = x @ w.T
+    return 1e-3 * out + 1e-6
+
+
+def linear_rows(x_bits: np.ndarray, blocks: np.ndarray, n: int, k: int,
+                rows: np.ndarray):
+    """(y, bound) restricted to the output columns `rows` (sampled checks)."""
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(n, k // QK, BLOCK_BYTES)
+    sub = b[np.asarray(rows)]
+    nr = sub.shape[0]
+    return linear(x_bits, sub, nr, k), error_bound(x_bits, sub, nr, k)
+
+
+# ------------------------------------------------------------------ quantizer
+def quantize(w: np.ndarray) -> np.ndarray:
+    """fp32 W [n, k] -> GGUF Q4_0 bytes [n, k/32, 18] by the rule in the header."""
+    w32 = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w32.shape
+    if k % QK:
+        raise ValueError("K must be a multiple of 32")
+    wb = w32.reshape(n, k // QK, QK)
+    idx = np.argmax(np.abs(wb), axis=2)                     # first maximum
+    amax = np.take_along_axis(wb, idx[:, :, None], axis=2)[:, :, 0]
+    d16 = (amax / np.float32(-8.0)).astype(np.float16)      # fp32 divide, RNE to fp16
+    df = d16.astype(np.float32)
+    zero = df == 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.rint(wb / df[:, :, None]) + np.float32(8.0)
+    r = np.clip(r, np.float32(0.0), np.float32(15.0))
+    r = np.where(zero[:, :, None], np.float32(8.0), r)
+    q = r.astype(np.uint8).reshape(n, k)
+    d16 = np.where(zero, np.float16(0.0), d16)
+    return gguf_encode(d16, q)
+
+
+# ----------------------------------------------------- device (packed) layout
+def padded_dims(n: int, k: int):
+    """(Np, Kp): rows rounded up to 16, columns up to 128."""
+    return -(-n // TILE_ROWS) * TILE_ROWS, -(-k // TILE_K) * TILE_K
+
+
+def packed_bytes(n: int, k: int) -> int:
+    np_, kp = padded_dims(n, k)
+    return np_ * (kp // QK) * BLOCK_BYTES
+
+
+def pack(blocks: np.ndarray, n: int, k: int) -> np.ndarray:
+    """GGUF bytes -> packed device layout, following include/q4_0.h.
+
+    Written as explicit index arithmetic over (row, block, k) so it can be
+    compared with the header text by eye:
+
+      nibble plane, super-tile (rt, kt) at byte ((rt * KT + kt) * 1024):
+        row n = 16 rt + r, block b = 4 kt + i, element e (0..31) of the block,
+        g = e // 8, j = e % 8:
+        byte offset within the tile = g * 256 + r * 16 + i * 4 + j // 2,
+        low nibble if j is even, high nibble if odd; stored value (q ^ 8).
+      scale plane, starting at Np * Kp / 2:
+        fp16 d of (n, b) at element index (rt * KT + kt) * 64 + r * 4 + i.
+    """
+    np_, kp = padded_dims(n, k)
+    d, q = gguf_decode(blocks, n, k)
+    qp = np.full((np_, kp), 8, dtype=np.uint8)
+    qp[:n, :k] = q
+    dp = np.zeros((np_, kp // QK), dtype=np.float16)
+    dp[:n, :k // QK] = d
+    kt_n = kp // TILE_K
+    nib = np.zeros(np_ * kp // 2, dtype=np.uint8)
+    sc = np.zeros(np_ * kp // QK, dtype=np.float16)
+    code = (qp ^ 8).astype(np.uint8)
+    # vectorised form of the loops described in the docstring
+    rows = np.arange(np_)
+    rt, r = rows // TILE_ROWS, rows % TILE_ROWS
+    for b in range(kp // QK):
+        kt, i = b // TILE_BLOCKS, b % TILE_BLOCKS
+        tile_base = (rt * kt_n + kt) * TILE_NIB_BYTES
+        for e in range(QK):
+            g, j = e // 8, e % 8
+            off = tile_base + g * 256 + r * 16 + i * 4 + j // 2
+            val = code[:, b * QK + e]
+            if j % 2 == 0:
+                nib[off] |= val
+            else:
+                nib[off] |= val << 4
+        sc[(rt * kt_n + kt) * 64 + r * 4 + i] = dp[:, b]
+    return np.concatenate([nib, sc.view(np.uint8)])
