@@ -1,0 +1,140 @@
+/*
+ * q4_0.h -- C ABI of libq4amd, a GGUF Q4_0 weight-only linear layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  The quantized Voxtral checkpoints store their linear
+ * weights as GGUF Q4_0 ("Voxtral Mini 4B Realtime (Rust) -- Shannon-Prime
+ * Fork", section "RTF Benchmark Results": "Voxtral Mini 4B Q4_0 GGUF"; hakusoku
+ * summary "Voxtral Mini 4B Realtime 概要", section "推論パス": "GGUF Q4_0"), and
+ * the Rust engine multiplies them with a shader that fuses dequantization into
+ * the matmul (hakusoku summary, section "線形演算・埋め込み").  The format:
+ * W is [N, K] (N outputs, K inputs, K a multiple of 32); each run of 32
+ * consecutive k of one row is a block of 18 bytes -- an fp16 scale d
+ * (little-endian) and 16 code bytes, byte j holding code q[j] in bits 0-3 and
+ * q[j+16] in bits 4-7 -- and a weight is w = (q - 8) * d.  The layer computes
+ *     y[m, n] = sum_k x[m, k] * w[n, k]
+ * with x bf16 [M, K] row-major and y fp32 [M, N] row-major (overwritten, no
+ * bias).  Fused QKV and fused gate/up projections (the Rust fork's TTS
+ * section lists "fused QKV+gate/up projections") share x between several
+ * weight matrices; q4_0_linear_multi does that in one launch.
+ *
+ * Conventions for every entry point.
+ *   - Pointers named as device memory must be device (or managed) memory on
+ *     the current HIP device; the caller owns every buffer.  The library
+ *     allocates nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call that
+ *     launches work is asynchronous on that stream; results are visible after
+ *     the caller synchronizes it.
+ *   - Every argument is checked before any HIP call.  On a bad argument the
+ *     call returns a nonzero q4_status and launches nothing.  A failed launch
+ *     returns Q4_ERR_HIP.  A device fault surfaces at the caller's next
+ *     synchronization.  Nothing aborts.
+ *   - Device pointers to x, y, packed, GGUF blocks and fp32 weights must be
+ *     16-byte aligned (any torch allocation is).  GGUF block buffers are
+ *     N * K/32 * 18 bytes, contiguous.
+ *   - Sizes: 1 <= N <= 2^30, 32 <= K <= 2^20, K % 32 == 0, 0 <= M <= 2^20.
+ *     M == 0 is a successful no-op.
+ */
+#ifndef Q4_0_H
+#define Q4_0_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    Q4_OK = 0,
+    Q4_ERR_NULL = 1,      /* a required pointer is NULL                       */
+    Q4_ERR_SHAPE = 2,     /* M, N or K out of range, or K % 32 != 0           */
+    Q4_ERR_ALIGN = 3,     /* a device pointer is not 16-byte aligned          */
+    Q4_ERR_SEGMENTS = 4,  /* nseg outside 1..8, or a bad segment entry        */
+    Q4_ERR_HIP = 5        /* the HIP runtime reported an error at launch      */
+} q4_status;
+
+/* Static English text for a status code (never NULL). */
+const char *q4_status_str(int status);
+
+/*
+ * Packed layout ("CDNA4 tiled Q4_0").  q4_0_pack rewrites GGUF blocks into
+ * this layout once, at load time; q4_0_linear reads only this layout.
+ *
+ *   Np = N rounded up to 16, Kp = K rounded up to 128, KT = Kp / 128.
+ *   Padding blocks have d = 0 and q = 8 (all their bytes are zero).
+ *   A super-tile covers 16 rows x 4 blocks (128 k).  Super-tile (rt, kt),
+ *   rt = n / 16, kt = b / 4 (b = k / 32), is stored at tile index
+ *   T = rt * KT + kt.
+ *
+ *   Nibble plane, bytes [0, Np * Kp / 2):
+ *     for row n = 16 rt + r, block b = 4 kt + i, element e = 8 g + j of the
+ *     block (g = 0..3, j = 0..7), the code (q XOR 8) -- the 4-bit two's
+ *     complement of q - 8 -- is at byte
+ *         T * 1024 + g * 256 + r * 16 + i * 4 + j / 2,
+ *     in the low nibble when j is even, the high nibble when j is odd.
+ *     So lane (16 g + r) of a 64-lane wave reading 16 bytes at lane * 16
+ *     receives, for blocks 4kt..4kt+3, elements 8g..8g+7 of row n, which is
+ *     the B-operand slice of a 16x16x32 bf16 MFMA for that row and k range.
+ *   Scale plane, bytes [Np * Kp / 2, Np * Kp / 2 + Np * Kp / 16):
+ *     fp16 d of (n, b) at element index T * 64 + r * 4 + i.
+ *
+ *   Total size: Np * (Kp / 32) * 18 bytes (equal to the GGUF size when no
+ *   padding is needed).
+ */
+size_t q4_0_packed_bytes(int64_t N, int64_t K);   /* 0 if N or K is invalid */
+
+/*
+ * Host-side quantizer counterpart, run on the device: fp32 W [N, K]
+ * (row-major, device) -> GGUF Q4_0 blocks (device, N * K/32 * 18 bytes).
+ * Per block: amax is the element of largest magnitude, keeping its sign
+ * (lowest index on ties); d = fp16(amax / -8) rounded to nearest even;
+ * q = clamp(rint(w / d) + 8, 0, 15), the division in fp32 and rint rounding
+ * half to even; if the fp16 d is zero the block stores d = +0 and q = 8.
+ * The pages quantize offline with scripts/quantize_tts_gguf.py (Rust fork,
+ * "Model Preparation"); the rule above is the GGUF Q4_0 reading of it.
+ * Inputs must be finite.  Bit-for-bit reproducible.
+ */
+q4_status q4_0_quantize(const float *w, int64_t N, int64_t K, void *gguf_blocks, void *stream);
+
+/* GGUF Q4_0 blocks (device) -> packed layout (device, q4_0_packed_bytes). */
+q4_status q4_0_pack(const void *gguf_blocks, int64_t N, int64_t K, void *packed, void *stream);
+
+/* Exact inverse of q4_0_pack (padding dropped); for tests and export. */
+q4_status q4_0_unpack(const void *packed, int64_t N, int64_t K, void *gguf_blocks, void *stream);
+
+/* Dequantize a packed matrix to fp32 W [N, K] (device): w = (q - 8) * d,
+ * exact in fp32.  For tests. */
+q4_status q4_0_dequant(const void *packed, int64_t N, int64_t K, float *w, void *stream);
+
+/*
+ * y[M, N] (fp32, device) = x[M, K] (bf16, device) times W^T, W packed.
+ * Accuracy: every product (q - 8) * x is formed exactly and scaled by d in
+ * fp32; y is within 1e-3 * sum_k |x_k * w_k| + 1e-6 of the exact result for
+ * any finite input whose result does not overflow fp32.  Deterministic:
+ * the same inputs give the same bits on every call (no atomics).
+ */
+q4_status q4_0_linear(const void *x_bf16, int64_t M, const void *packed, int64_t N, int64_t K,
+                      float *y, void *stream);
+
+/* One weight matrix of a fused launch: packed weights [N, K], output y [M, N]. */
+typedef struct {
+    const void *packed;
+    int64_t N;
+    float *y;
+} q4_0_segment;
+
+/*
+ * Several weight matrices sharing x and K in one launch (fused QKV: three
+ * segments 4096/1024/1024; fused gate/up: two of 9216).  `segs` is host
+ * memory with nseg entries, 1 <= nseg <= 8; each segment is validated like a
+ * q4_0_linear call.  Equal, segment by segment, to separate q4_0_linear calls.
+ */
+q4_status q4_0_linear_multi(const void *x_bf16, int64_t M, int64_t K, const q4_0_segment *segs,
+                            int nseg, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_0_H */

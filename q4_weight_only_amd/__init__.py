@@ -1,1 +1,23 @@
-"""MI355X-native GGUF Q4_0 weight-only linear layer (HIP kernels behind a C ABI)."""
+"""MI355X-native GGUF Q4_0 weight-only linear layer.
+
+The computation lives in libq4amd.so (HIP kernels for gfx950 behind the C ABI
+of include/q4_0.h); this package is its thin Python binding.  The library is
+loaded on first use and a missing build raises instead of falling back.
+"""
+
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    PackedWeight,
+    Q4Error,
+    dequant,
+    gguf_bytes,
+    lib,
+    library_path,
+    linear,
+    linear_multi,
+    pack,
+    packed_bytes,
+    quantize,
+    status_str,
+    unpack,
+)

@@ -1,0 +1,204 @@
+"""ctypes binding of libq4amd (include/q4_0.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  PyTorch provides device memory and the current stream.  If the
+library has not been built the first call raises; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq4amd.so")
+_lib = None
+_lock = threading.Lock()
+
+Q4_OK = 0
+STATUS_NAMES = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIGN",
+                4: "Q4_ERR_SEGMENTS", 5: "Q4_ERR_HIP"}
+EXPORTS = ("q4_status_str", "q4_0_packed_bytes", "q4_0_quantize", "q4_0_pack", "q4_0_unpack",
+           "q4_0_dequant", "q4_0_linear", "q4_0_linear_multi")
+
+
+class Q4Error(ValueError):
+    """A nonzero q4_status from the library."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({status_str(status)})")
+
+
+class Segment(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("N", ctypes.c_int64), ("y", ctypes.c_void_p)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libq4amd.so (once); raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise RuntimeError(
+                    f"{_LIB_PATH} is not built; run `python -m q4_weight_only_amd.build` "
+                    "(or __graft_entry__.build()) first")
+            L = ctypes.CDLL(_LIB_PATH)
+            vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+            L.q4_status_str.argtypes = [i32]
+            L.q4_status_str.restype = ctypes.c_char_p
+            L.q4_0_packed_bytes.argtypes = [i64, i64]
+            L.q4_0_packed_bytes.restype = ctypes.c_size_t
+            for name in ("q4_0_quantize", "q4_0_pack", "q4_0_unpack", "q4_0_dequant"):
+                fn = getattr(L, name)
+                fn.argtypes = [vp, i64, i64, vp, vp]
+                fn.restype = i32
+            L.q4_0_linear.argtypes = [vp, i64, vp, i64, i64, vp, vp]
+            L.q4_0_linear.restype = i32
+            L.q4_0_linear_multi.argtypes = [vp, i64, i64, ctypes.POINTER(Segment), i32, vp]
+            L.q4_0_linear_multi.restype = i32
+            _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().q4_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != Q4_OK:
+        raise Q4Error(status, what)
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA/HIP tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ------------------------------------------------------------------ API
+def packed_bytes(n: int, k: int) -> int:
+    return int(lib().q4_0_packed_bytes(int(n), int(k)))
+
+
+def gguf_bytes(n: int, k: int) -> int:
+    return int(n) * (int(k) // 32) * 18
+
+
+class PackedWeight:
+    """A Q4_0 weight matrix [N, K] in the packed device layout."""
+
+    __slots__ = ("data", "n", "k")
+
+    def __init__(self, data: torch.Tensor, n: int, k: int):
+        self.data, self.n, self.k = data, int(n), int(k)
+
+    @property
+    def device(self) -> torch.device:
+        return self.data.device
+
+
+def quantize(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 W [N, K] on the device -> GGUF Q4_0 bytes [N, K/32, 18] (uint8)."""
+    _dev(w, "w", torch.float32)
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    n, k = w.shape
+    if out is None:
+        out = torch.empty((n, max(k // 32, 0), 18), dtype=torch.uint8, device=w.device)
+    _dev(out, "out", torch.uint8)
+    if out.numel() != gguf_bytes(n, k):
+        raise ValueError("out has the wrong size")
+    with torch.cuda.device(w.device):
+        _check(lib().q4_0_quantize(w.data_ptr(), n, k, out.data_ptr(), _stream(w.device)), "q4_0_quantize")
+    return out
+
+
+def pack(blocks: torch.Tensor, n: int, k: int, out: torch.Tensor | None = None) -> PackedWeight:
+    """GGUF Q4_0 bytes (uint8, N*K/32*18 elements, on the device) -> PackedWeight."""
+    _dev(blocks, "blocks", torch.uint8)
+    if blocks.numel() != gguf_bytes(n, k):
+        raise ValueError(f"blocks must hold {gguf_bytes(n, k)} bytes for [{n}, {k}]")
+    nbytes = packed_bytes(n, k)
+    if nbytes == 0:
+        raise ValueError(f"invalid shape [{n}, {k}]")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=blocks.device)
+    _dev(out, "out", torch.uint8)
+    if out.numel() != nbytes:
+        raise ValueError("out has the wrong size")
+    with torch.cuda.device(blocks.device):
+        _check(lib().q4_0_pack(blocks.data_ptr(), n, k, out.data_ptr(), _stream(blocks.device)), "q4_0_pack")
+    return PackedWeight(out, n, k)
+
+
+def unpack(pw: PackedWeight) -> torch.Tensor:
+    out = torch.empty((pw.n, pw.k // 32, 18), dtype=torch.uint8, device=pw.device)
+    with torch.cuda.device(pw.device):
+        _check(lib().q4_0_unpack(pw.data.data_ptr(), pw.n, pw.k, out.data_ptr(), _stream(pw.device)),
+               "q4_0_unpack")
+    return out
+
+
+def dequant(pw: PackedWeight) -> torch.Tensor:
+    out = torch.empty((pw.n, pw.k), dtype=torch.float32, device=pw.device)
+    with torch.cuda.device(pw.device):
+        _check(lib().q4_0_dequant(pw.data.data_ptr(), pw.n, pw.k, out.data_ptr(), _stream(pw.device)),
+               "q4_0_dequant")
+    return out
+
+
+def linear(x: torch.Tensor, pw: PackedWeight, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y [M, N] fp32 = x [M, K] bf16 times W^T."""
+    _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2 or x.shape[1] != pw.k:
+        raise ValueError(f"x must be [M, {pw.k}]")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, pw.n), dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    if tuple(out.shape) != (m, pw.n):
+        raise ValueError("out has the wrong shape")
+    with torch.cuda.device(x.device):
+        _check(lib().q4_0_linear(x.data_ptr(), m, pw.data.data_ptr(), pw.n, pw.k, out.data_ptr(),
+                                 _stream(x.device)), "q4_0_linear")
+    return out
+
+
+def linear_multi(x: torch.Tensor, weights, outs=None):
+    """One launch over several weight matrices sharing x: returns [y_i]."""
+    _dev(x, "x", torch.bfloat16)
+    weights = list(weights)
+    if not 1 <= len(weights) <= 8:
+        raise ValueError("need 1..8 weight matrices")
+    k = x.shape[1]
+    m = x.shape[0]
+    if outs is None:
+        outs = [torch.empty((m, w.n), dtype=torch.float32, device=x.device) for w in weights]
+    segs = (Segment * len(weights))()
+    for i, (w, y) in enumerate(zip(weights, outs)):
+        if w.k != k:
+            raise ValueError("all segments must share K")
+        _dev(y, f"outs[{i}]", torch.float32)
+        if tuple(y.shape) != (m, w.n):
+            raise ValueError(f"outs[{i}] has the wrong shape")
+        segs[i] = Segment(w.data.data_ptr(), w.n, y.data_ptr())
+    with torch.cuda.device(x.device):
+        _check(lib().q4_0_linear_multi(x.data_ptr(), m, k, segs, len(weights), _stream(x.device)),
+               "q4_0_linear_multi")
+    return outs

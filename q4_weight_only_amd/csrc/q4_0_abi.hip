@@ -1,0 +1,122 @@
+// extern "C" entry points of libq4amd (declared in include/q4_0.h).
+// Every argument is validated here, before any HIP call, so the error paths
+// are testable without a GPU.
+
+#include "q4_0.h"
+
+#include "q4_0_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxN = int64_t(1) << 30;
+constexpr int64_t kMaxK = int64_t(1) << 20;
+constexpr int64_t kMaxM = int64_t(1) << 20;
+
+bool shape_ok(int64_t N, int64_t K) {
+    return N >= 1 && N <= kMaxN && K >= q4::kQK && K <= kMaxK && K % q4::kQK == 0;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+q4_status from_hip(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_ERR_HIP; }
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+q4::Segment make_segment(const void *packed, int64_t N, int64_t K, float *y) {
+    const q4::PackedDims pd(N, K);
+    q4::Segment sg;
+    sg.nib = static_cast<const uint8_t *>(packed);
+    sg.scales = reinterpret_cast<const uint16_t *>(static_cast<const uint8_t *>(packed) + pd.nib_bytes());
+    sg.y = y;
+    sg.N = static_cast<int32_t>(N);
+    sg.RT = static_cast<int32_t>(pd.RT);
+    sg.tile_begin = 0;
+    return sg;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *q4_status_str(int status) {
+    switch (status) {
+        case Q4_OK: return "ok";
+        case Q4_ERR_NULL: return "a required pointer is NULL";
+        case Q4_ERR_SHAPE: return "shape out of range (need 1<=N<=2^30, 32<=K<=2^20, K%32==0, 0<=M<=2^20)";
+        case Q4_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+        case Q4_ERR_SEGMENTS: return "bad segment list (need 1<=nseg<=8 and valid entries)";
+        case Q4_ERR_HIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+size_t q4_0_packed_bytes(int64_t N, int64_t K) {
+    if (!shape_ok(N, K)) return 0;
+    return static_cast<size_t>(q4::PackedDims(N, K).total_bytes());
+}
+
+q4_status q4_0_quantize(const float *w, int64_t N, int64_t K, void *gguf_blocks, void *stream) {
+    if (!shape_ok(N, K)) return Q4_ERR_SHAPE;
+    if (!w || !gguf_blocks) return Q4_ERR_NULL;
+    if (!aligned16(w) || !aligned16(gguf_blocks)) return Q4_ERR_ALIGN;
+    return from_hip(q4::launch_quantize(w, N, K, static_cast<uint8_t *>(gguf_blocks), as_stream(stream)));
+}
+
+q4_status q4_0_pack(const void *gguf_blocks, int64_t N, int64_t K, void *packed, void *stream) {
+    if (!shape_ok(N, K)) return Q4_ERR_SHAPE;
+    if (!gguf_blocks || !packed) return Q4_ERR_NULL;
+    if (!aligned16(gguf_blocks) || !aligned16(packed)) return Q4_ERR_ALIGN;
+    return from_hip(q4::launch_pack(static_cast<const uint8_t *>(gguf_blocks), N, K,
+                                    static_cast<uint8_t *>(packed), as_stream(stream)));
+}
+
+q4_status q4_0_unpack(const void *packed, int64_t N, int64_t K, void *gguf_blocks, void *stream) {
+    if (!shape_ok(N, K)) return Q4_ERR_SHAPE;
+    if (!gguf_blocks || !packed) return Q4_ERR_NULL;
+    if (!aligned16(gguf_blocks) || !aligned16(packed)) return Q4_ERR_ALIGN;
+    return from_hip(q4::launch_unpack(static_cast<const uint8_t *>(packed), N, K,
+                                      static_cast<uint8_t *>(gguf_blocks), as_stream(stream)));
+}
+
+q4_status q4_0_dequant(const void *packed, int64_t N, int64_t K, float *w, void *stream) {
+    if (!shape_ok(N, K)) return Q4_ERR_SHAPE;
+    if (!w || !packed) return Q4_ERR_NULL;
+    if (!aligned16(w) || !aligned16(packed)) return Q4_ERR_ALIGN;
+    return from_hip(q4::launch_dequant(static_cast<const uint8_t *>(packed), N, K, w, as_stream(stream)));
+}
+
+q4_status q4_0_linear(const void *x_bf16, int64_t M, const void *packed, int64_t N, int64_t K, float *y,
+                      void *stream) {
+    q4_0_segment seg;
+    seg.packed = packed;
+    seg.N = N;
+    seg.y = y;
+    return q4_0_linear_multi(x_bf16, M, K, &seg, 1, stream);
+}
+
+q4_status q4_0_linear_multi(const void *x_bf16, int64_t M, int64_t K, const q4_0_segment *segs, int nseg,
+                            void *stream) {
+    if (!segs) return Q4_ERR_NULL;
+    if (nseg < 1 || nseg > q4::kMaxSegments) return Q4_ERR_SEGMENTS;
+    if (M < 0 || M > kMaxM) return Q4_ERR_SHAPE;
+    for (int i = 0; i < nseg; ++i)
+        if (!shape_ok(segs[i].N, K)) return Q4_ERR_SHAPE;
+    if (M == 0) return Q4_OK;
+    if (!x_bf16) return Q4_ERR_NULL;
+    if (!aligned16(x_bf16)) return Q4_ERR_ALIGN;
+    for (int i = 0; i < nseg; ++i) {
+        if (!segs[i].packed || !segs[i].y) return Q4_ERR_NULL;
+        if (!aligned16(segs[i].packed) || !aligned16(segs[i].y)) return Q4_ERR_ALIGN;
+    }
+    q4::LinearArgs a;
+    a.x = static_cast<const uint16_t *>(x_bf16);
+    a.M = static_cast<int32_t>(M);
+    a.K = static_cast<int32_t>(K);
+    a.KT = static_cast<int32_t>(q4::round_up(K, q4::kTileK) / q4::kTileK);
+    a.nseg = nseg;
+    for (int i = 0; i < q4::kMaxSegments; ++i) a.seg[i] = q4::Segment{};
+    for (int i = 0; i < nseg; ++i) a.seg[i] = make_segment(segs[i].packed, segs[i].N, K, segs[i].y);
+    return from_hip(q4::launch_linear(a, as_stream(stream)));
+}
+
+}  // extern "C"

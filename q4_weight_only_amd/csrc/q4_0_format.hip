@@ -1,0 +1,222 @@
+// Format kernels: quantize (fp32 -> GGUF Q4_0), pack (GGUF -> CDNA4 tiled
+// layout), unpack (inverse) and dequant (packed -> fp32).  All are one-time or
+// test-only steps outside the linear's hot loop; they are written for
+// straightforward coalescing rather than peak bandwidth.
+//
+// GGUF Q4_0 block (the format of the quantized Voxtral checkpoints, named in
+// the Rust fork's "RTF Benchmark Results"): 2 bytes fp16 d, then 16 bytes;
+// byte j holds code q[j] (bits 0-3) and q[j+16] (bits 4-7); w = (q - 8) * d.
+// The packed layout is defined in include/q4_0.h.
+
+#include <hip/hip_fp16.h>
+
+#include "q4_0_internal.h"
+
+namespace q4 {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Read one 18-byte GGUF block (2-byte aligned) as 9 halfwords.
+__device__ inline void load_gguf_block(const uint8_t *p, uint16_t &d, uint8_t q[32]) {
+    const uint16_t *h = reinterpret_cast<const uint16_t *>(p);
+    d = h[0];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const uint16_t v = h[1 + t];
+        const uint8_t b0 = v & 0xFF, b1 = v >> 8;     // code bytes 2t and 2t+1
+        q[2 * t] = b0 & 0xF;
+        q[2 * t + 16] = b0 >> 4;
+        q[2 * t + 1] = b1 & 0xF;
+        q[2 * t + 17] = b1 >> 4;
+    }
+}
+
+__device__ inline void store_gguf_block(uint8_t *p, uint16_t d, const uint8_t q[32]) {
+    uint16_t *h = reinterpret_cast<uint16_t *>(p);
+    h[0] = d;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const uint32_t b0 = q[2 * t] | (q[2 * t + 16] << 4);
+        const uint32_t b1 = q[2 * t + 1] | (q[2 * t + 17] << 4);
+        h[1 + t] = static_cast<uint16_t>(b0 | (b1 << 8));
+    }
+}
+
+// --------------------------------------------------------------- quantize
+// One thread per GGUF block (row n, block b); the block's 32 floats are
+// contiguous at w + (n * K + 32 b), i.e. at w + 32 * (n * K/32 + b).
+__global__ __launch_bounds__(kThreads) void quantize_kernel(const float *__restrict__ w,
+                                                            int64_t nblocks,
+                                                            uint8_t *__restrict__ out) {
+    const int64_t idx = blockIdx.x * (int64_t)kThreads + threadIdx.x;
+    if (idx >= nblocks) return;
+    const float4 *src = reinterpret_cast<const float4 *>(w + idx * kQK);
+    float v[32];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const float4 f = src[t];
+        v[4 * t] = f.x;
+        v[4 * t + 1] = f.y;
+        v[4 * t + 2] = f.z;
+        v[4 * t + 3] = f.w;
+    }
+    // signed element of largest magnitude; strict '>' keeps the first one
+    float amax = v[0];
+#pragma unroll
+    for (int j = 1; j < 32; ++j)
+        if (fabsf(v[j]) > fabsf(amax)) amax = v[j];
+    const __half d16 = __float2half_rn(amax / -8.0f);
+    const float df = __half2float(d16);
+    uint8_t q[32];
+    uint16_t dbits;
+    if (df == 0.0f) {
+        dbits = 0;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) q[j] = 8;
+    } else {
+        dbits = __half_as_ushort(d16);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            float r = rintf(v[j] / df) + 8.0f;   // IEEE fp32 divide, ties to even
+            r = fminf(fmaxf(r, 0.0f), 15.0f);
+            q[j] = static_cast<uint8_t>(r);
+        }
+    }
+    store_gguf_block(out + idx * kBlockBytes, dbits, q);
+}
+
+// ------------------------------------------------------------------- pack
+// One thread per (row, block) of the padded matrix.  Thread t works on
+// super-tile T = t / 64 and entry e = t % 64 = 4 r + i (row r, block i of the
+// tile); for each k-group g its 4-byte piece goes to
+// T * 1024 + g * 256 + e * 4, so a wave writes four contiguous 256-byte runs.
+__global__ __launch_bounds__(kThreads) void pack_kernel(const uint8_t *__restrict__ gguf, int32_t N,
+                                                        int32_t K, int32_t KT, int64_t nentries,
+                                                        uint8_t *__restrict__ nib,
+                                                        uint16_t *__restrict__ scales) {
+    const int64_t t = blockIdx.x * (int64_t)kThreads + threadIdx.x;
+    if (t >= nentries) return;
+    const int64_t T = t >> 6;
+    const int e = static_cast<int>(t & 63);
+    const int r = e >> 2, i = e & 3;
+    const int64_t rt = T / KT, kt = T % KT;
+    const int64_t n = rt * kTileRows + r;
+    const int64_t b = kt * kTileBlocks + i;
+    uint16_t d = 0;
+    uint8_t q[32];
+    if (n < N && b < K / kQK) {
+        load_gguf_block(gguf + (n * (K / kQK) + b) * kBlockBytes, d, q);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) q[j] = 8;
+    }
+    uint32_t *dst = reinterpret_cast<uint32_t *>(nib + T * kTileNibBytes);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        uint32_t piece = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) piece |= static_cast<uint32_t>(q[8 * g + j] ^ 8) << (4 * j);
+        dst[g * 64 + e] = piece;
+    }
+    scales[T * kTileScales + e] = d;
+}
+
+// ----------------------------------------------------------------- unpack
+__global__ __launch_bounds__(kThreads) void unpack_kernel(const uint8_t *__restrict__ nib,
+                                                          const uint16_t *__restrict__ scales,
+                                                          int32_t N, int32_t K, int32_t KT,
+                                                          int64_t nentries,
+                                                          uint8_t *__restrict__ gguf) {
+    const int64_t t = blockIdx.x * (int64_t)kThreads + threadIdx.x;
+    if (t >= nentries) return;
+    const int64_t T = t >> 6;
+    const int e = static_cast<int>(t & 63);
+    const int r = e >> 2, i = e & 3;
+    const int64_t rt = T / KT, kt = T % KT;
+    const int64_t n = rt * kTileRows + r;
+    const int64_t b = kt * kTileBlocks + i;
+    if (n >= N || b >= K / kQK) return;
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(nib + T * kTileNibBytes);
+    uint8_t q[32];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint32_t piece = src[g * 64 + e];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) q[8 * g + j] = ((piece >> (4 * j)) & 0xF) ^ 8;
+    }
+    store_gguf_block(gguf + (n * (K / kQK) + b) * kBlockBytes, scales[T * kTileScales + e], q);
+}
+
+// ---------------------------------------------------------------- dequant
+// One thread per real (row, block); writes 32 floats w[n, 32 b .. 32 b + 31].
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__restrict__ nib,
+                                                           const uint16_t *__restrict__ scales,
+                                                           int32_t N, int32_t K, int32_t KT,
+                                                           int64_t nentries,
+                                                           float *__restrict__ w) {
+    const int64_t t = blockIdx.x * (int64_t)kThreads + threadIdx.x;
+    if (t >= nentries) return;
+    const int64_t T = t >> 6;
+    const int e = static_cast<int>(t & 63);
+    const int r = e >> 2, i = e & 3;
+    const int64_t rt = T / KT, kt = T % KT;
+    const int64_t n = rt * kTileRows + r;
+    const int64_t b = kt * kTileBlocks + i;
+    if (n >= N || b >= K / kQK) return;
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(nib + T * kTileNibBytes);
+    const float d = __half2float(__ushort_as_half(scales[T * kTileScales + e]));
+    float4 *dst = reinterpret_cast<float4 *>(w + n * K + b * kQK);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint32_t piece = src[g * 64 + e];
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            // sign-extend the 4-bit code: it is q - 8 in two's complement
+            const int s = static_cast<int>(piece << (28 - 4 * j)) >> 28;
+            v[j] = static_cast<float>(s) * d;
+        }
+        dst[2 * g] = make_float4(v[0], v[1], v[2], v[3]);
+        dst[2 * g + 1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+}
+
+inline dim3 grid_for(int64_t n) { return dim3(static_cast<unsigned>((n + kThreads - 1) / kThreads)); }
+
+}  // namespace
+
+hipError_t launch_quantize(const float *w, int64_t N, int64_t K, uint8_t *out, hipStream_t s) {
+    const int64_t nblocks = N * (K / kQK);
+    hipLaunchKernelGGL(quantize_kernel, grid_for(nblocks), dim3(kThreads), 0, s, w, nblocks, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack(const uint8_t *gguf, int64_t N, int64_t K, uint8_t *packed, hipStream_t s) {
+    const PackedDims pd(N, K);
+    const int64_t nentries = pd.RT * pd.KT * 64;
+    hipLaunchKernelGGL(pack_kernel, grid_for(nentries), dim3(kThreads), 0, s, gguf, (int32_t)N,
+                       (int32_t)K, (int32_t)pd.KT, nentries, packed,
+                       reinterpret_cast<uint16_t *>(packed + pd.nib_bytes()));
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint8_t *packed, int64_t N, int64_t K, uint8_t *gguf, hipStream_t s) {
+    const PackedDims pd(N, K);
+    const int64_t nentries = pd.RT * pd.KT * 64;
+    hipLaunchKernelGGL(unpack_kernel, grid_for(nentries), dim3(kThreads), 0, s, packed,
+                       reinterpret_cast<const uint16_t *>(packed + pd.nib_bytes()), (int32_t)N,
+                       (int32_t)K, (int32_t)pd.KT, nentries, gguf);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t *packed, int64_t N, int64_t K, float *w, hipStream_t s) {
+    const PackedDims pd(N, K);
+    const int64_t nentries = pd.RT * pd.KT * 64;
+    hipLaunchKernelGGL(dequant_kernel, grid_for(nentries), dim3(kThreads), 0, s, packed,
+                       reinterpret_cast<const uint16_t *>(packed + pd.nib_bytes()), (int32_t)N,
+                       (int32_t)K, (int32_t)pd.KT, nentries, w);
+    return hipGetLastError();
+}
+
+}  // namespace q4

@@ -1,0 +1,60 @@
+// Internal declarations shared by the host-side ABI and the kernel files.
+// Not part of the public ABI (that is include/q4_0.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+// Layout constants of the packed ("CDNA4 tiled") Q4_0 format.
+constexpr int kQK = 32;            // weights per block
+constexpr int kBlockBytes = 18;    // fp16 d + 16 code bytes (GGUF)
+constexpr int kTileRows = 16;      // rows per super-tile
+constexpr int kTileBlocks = 4;     // blocks per super-tile
+constexpr int kTileK = 128;        // k per super-tile
+constexpr int kTileNibBytes = 1024;
+constexpr int kTileScales = 64;    // fp16 scales per super-tile
+constexpr int kMaxSegments = 8;
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+struct PackedDims {
+    int64_t N, K, Np, Kp, KT, RT;
+    explicit PackedDims(int64_t n, int64_t k)
+        : N(n), K(k), Np(round_up(n, kTileRows)), Kp(round_up(k, kTileK)),
+          KT(round_up(k, kTileK) / kTileK), RT(round_up(n, kTileRows) / kTileRows) {}
+    int64_t nib_bytes() const { return Np * Kp / 2; }
+    int64_t total_bytes() const { return Np * (Kp / kQK) * kBlockBytes; }
+};
+
+// One weight matrix of a (possibly fused) launch, as the kernels see it.
+struct Segment {
+    const uint8_t *nib;      // nibble plane
+    const uint16_t *scales;  // scale plane (fp16 bits)
+    float *y;                // [M, N] row-major
+    int32_t N;               // true rows of W (= columns of y)
+    int32_t RT;              // padded rows / 16
+    int32_t tile_begin;      // first work tile of this segment in the launch
+};
+
+struct LinearArgs {
+    const uint16_t *x;       // bf16 bits [M, K]
+    int32_t M;
+    int32_t K;               // true K (multiple of 32)
+    int32_t KT;              // padded K / 128
+    int32_t nseg;
+    Segment seg[kMaxSegments];
+};
+
+// Launchers (return hipError_t from the launch).
+hipError_t launch_quantize(const float *w, int64_t N, int64_t K, uint8_t *out, hipStream_t s);
+hipError_t launch_pack(const uint8_t *gguf, int64_t N, int64_t K, uint8_t *packed, hipStream_t s);
+hipError_t launch_unpack(const uint8_t *packed, int64_t N, int64_t K, uint8_t *gguf, hipStream_t s);
+hipError_t launch_dequant(const uint8_t *packed, int64_t N, int64_t K, float *w, hipStream_t s);
+
+// Runs the fused linear over all segments of `a` (segments' tile_begin is
+// filled in by the launcher).
+hipError_t launch_linear(LinearArgs a, hipStream_t s);
+
+}  // namespace q4

@@ -66,3 +66,67 @@ def decoder_layer_ops():
         ("gate_up", DECODER_DIM, GATE_UP_SEGMENTS),
         ("down", FFN_DIM, (DECODER_DIM,)),
     )
+
+
+# ------------------------------------------------------------ workloads
+class LinearSpec:
+    """One launch of a workload: segment row counts share K and x."""
+
+    __slots__ = ("name", "K", "Ns", "w_tags", "x_tags")
+
+    def __init__(self, name, K, Ns, w_tags, x_tags):
+        self.name, self.K, self.Ns = name, int(K), tuple(int(n) for n in Ns)
+        self.w_tags = tuple(tuple(t) for t in w_tags)   # one tag tuple per segment
+        self.x_tags = tuple(x_tags)
+
+    def weight(self, seg: int, seed: int = 0) -> np.ndarray:
+        return weights_f32((self.Ns[seg], self.K), seed=seed, tags=self.w_tags[seg])
+
+    def activations(self, m: int, seed: int = 0) -> np.ndarray:
+        return activations_bf16((m, self.K), seed=seed, tags=self.x_tags + (m,))
+
+    def weight_bytes(self) -> int:
+        return sum(n * (self.K // 32) * 18 for n in self.Ns)
+
+
+def _decoder_specs(cfg: int, layers):
+    out = []
+    for layer in layers:
+        for op, (name, k, ns) in enumerate(decoder_layer_ops()):
+            out.append(LinearSpec(f"L{layer}.{name}", k, ns,
+                                  [(2, layer, op, s) for s in range(len(ns))], (cfg, layer, op)))
+    return out
+
+
+def workload(cfg: int):
+    """(description, [(LinearSpec, (M, ...))]) for the five workloads.
+
+    1  one GEMV: M=1, K=3072, N=4096
+    2  a decoder layer's decode step, 26 layers of distinct weights, M in {1, 2}:
+       fused QKV 3072->4096+1024+1024, O 4096->3072, fused gate/up
+       3072->9216+9216, down 9216->3072
+    3  LM head K=3072, N=131072, M in {1, 32}
+    4  prefill M=2048 through the four decoder shapes (layer-0 weights of 2)
+    5  audio side: adapter 5120->3072 and 3072->3072 at M=1505, encoder
+       1280->5120 and 5120->1280 at M=6020
+    """
+    if cfg == 1:
+        return ("single Q4_0 GEMV M=1 K=3072 N=4096",
+                [(LinearSpec("gemv", 3072, (4096,), [(1, 0, 0, 0)], (1, 0, 0)), (1,))])
+    if cfg == 2:
+        return ("26-layer decoder decode step, M=1 and M=2",
+                [(s, (1, 2)) for s in _decoder_specs(2, range(DECODER_LAYERS))])
+    if cfg == 3:
+        return ("LM head K=3072 N=131072, M=1 and M=32",
+                [(LinearSpec("lm_head", DECODER_DIM, (VOCAB,), [(3, 0, 0, 0)], (3, 0, 0)), (1, 32))])
+    if cfg == 4:
+        return ("prefill M=2048 through the decoder shapes",
+                [(s, (2048,)) for s in _decoder_specs(4, [0])])
+    if cfg == 5:
+        return ("audio linears: adapter at M=1505, encoder at M=6020", [
+            (LinearSpec("adapter", 5120, (3072,), [(5, 0, 0, 0)], (5, 0, 0)), (1505,)),
+            (LinearSpec("adapter_out", 3072, (3072,), [(5, 0, 1, 0)], (5, 0, 1)), (1505,)),
+            (LinearSpec("enc_up", 1280, (5120,), [(5, 0, 2, 0)], (5, 0, 2)), (6020,)),
+            (LinearSpec("enc_down", 5120, (1280,), [(5, 0, 3, 0)], (5, 0, 3)), (6020,)),
+        ])
+    raise ValueError(f"no workload {cfg}")

@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/q4_0.h declares, sizes its buffers as documented, and rejects bad
+arguments before touching the HIP runtime.
+
+Only argument combinations that fail validation (or M == 0) are passed, so no
+kernel is ever launched here; fake device addresses are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import q4_0_oracle as O
+import q4_weight_only_amd as q4
+from q4_weight_only_amd import _binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "q4_0.h")
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+MISALIGNED = 0x10004
+
+OK, NULL, SHAPE, ALIGN, SEGS = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(q4.library_path()):
+        import subprocess, sys
+        subprocess.run([sys.executable, "-m", "q4_weight_only_amd.build"], check=True)
+    return q4.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4_\w+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(L):
+    names = _declared_functions()
+    assert len(names) >= 8
+    for name in names:
+        assert hasattr(L, name), name
+    assert sorted(B.EXPORTS) == names
+
+
+def test_status_strings(L):
+    for s in range(6):
+        assert q4.status_str(s) and q4.status_str(s) != "unknown status"
+    assert q4.status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("n,k", [(4096, 3072), (131072, 3072), (40, 384), (1, 32), (17, 96), (6020, 1280)])
+def test_packed_bytes_matches_layout_definition(L, n, k):
+    assert q4.packed_bytes(n, k) == O.packed_bytes(n, k)
+
+
+@pytest.mark.parametrize("n,k", [(0, 32), (-1, 64), (16, 0), (16, 31), (16, 48), (2**30 + 1, 32), (16, 2**20 + 32)])
+def test_packed_bytes_invalid_is_zero(L, n, k):
+    assert q4.packed_bytes(n, k) == 0
+
+
+@pytest.mark.parametrize("fn", ["q4_0_quantize", "q4_0_pack", "q4_0_unpack", "q4_0_dequant"])
+def test_format_entry_points_validate_first(L, fn):
+    f = getattr(L, fn)
+    assert f(FAKE, 16, 48, FAKE, None) == SHAPE
+    assert f(FAKE, 0, 64, FAKE, None) == SHAPE
+    assert f(None, 16, 64, FAKE, None) == NULL
+    assert f(FAKE, 16, 64, None, None) == NULL
+    assert f(MISALIGNED, 16, 64, FAKE, None) == ALIGN
+    assert f(FAKE, 16, 64, MISALIGNED, None) == ALIGN
+
+
+def test_linear_validates_first(L):
+    lin = L.q4_0_linear
+    assert lin(FAKE, 1, FAKE, 16, 48, FAKE, None) == SHAPE        # K % 32
+    assert lin(FAKE, -1, FAKE, 16, 64, FAKE, None) == SHAPE       # M < 0
+    assert lin(FAKE, 2**20 + 1, FAKE, 16, 64, FAKE, None) == SHAPE
+    assert lin(FAKE, 1, FAKE, 0, 64, FAKE, None) == SHAPE
+    assert lin(None, 1, FAKE, 16, 64, FAKE, None) == NULL
+    assert lin(FAKE, 1, None, 16, 64, FAKE, None) == NULL
+    assert lin(FAKE, 1, FAKE, 16, 64, None, None) == NULL
+    assert lin(MISALIGNED, 1, FAKE, 16, 64, FAKE, None) == ALIGN
+    assert lin(FAKE, 1, MISALIGNED, 16, 64, FAKE, None) == ALIGN
+    assert lin(FAKE, 1, FAKE, 16, 64, MISALIGNED, None) == ALIGN
+    # M == 0 is a successful no-op, even with NULL pointers
+    assert lin(None, 0, None, 16, 64, None, None) == OK
+
+
+def test_linear_multi_validates_first(L):
+    segs = (B.Segment * 9)()
+    for i in range(9):
+        segs[i] = B.Segment(FAKE, 16, FAKE)
+    multi = L.q4_0_linear_multi
+    assert multi(FAKE, 1, 64, None, 1, None) == NULL
+    assert multi(FAKE, 1, 64, segs, 0, None) == SEGS
+    assert multi(FAKE, 1, 64, segs, 9, None) == SEGS
+    bad = (B.Segment * 3)(B.Segment(FAKE, 16, FAKE), B.Segment(FAKE, 0, FAKE), B.Segment(FAKE, 16, FAKE))
+    assert multi(FAKE, 1, 64, bad, 3, None) == SHAPE
+    nul = (B.Segment * 2)(B.Segment(FAKE, 16, FAKE), B.Segment(None, 16, FAKE))
+    assert multi(FAKE, 1, 64, nul, 2, None) == NULL
+    mis = (B.Segment * 2)(B.Segment(FAKE, 16, FAKE), B.Segment(FAKE, 16, MISALIGNED))
+    assert multi(FAKE, 1, 64, mis, 2, None) == ALIGN
+    assert multi(FAKE, 1, 48, segs, 2, None) == SHAPE
+    assert multi(None, 0, 64, segs, 8, None) == OK
+
+
+def test_python_binding_raises_on_bad_status(L):
+    with pytest.raises(q4.Q4Error) as ei:
+        B._check(SHAPE, "q4_0_linear")
+    assert ei.value.status == SHAPE and "Q4_ERR_SHAPE" in str(ei.value)
+
+
+def test_product_path_has_no_oracle_dependency():
+    """The package never imports the oracle (it is test infrastructure)."""
+    pkg = os.path.dirname(q4.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(root, f), encoding="utf-8").read()
+                assert "import oracle" not in src and "from oracle" not in src, f

@@ -1,0 +1,142 @@
+"""Parity of the device linear with the oracle on sizes the oracle finishes in
+seconds: every output element within 1e-3 * sum|x w| + 1e-6, across the
+kernel variants (M = 1, 2, 3-4, 5-16, 17-32, > 32), several tiles in N and K,
+ragged edges, structured weights, fused segments and determinism."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import q4_0_oracle as O
+import q4_weight_only_amd as q4
+from q4_weight_only_amd import inputs
+
+from gpu_helpers import DEV, assert_within_bound, device_weight_from_blocks, device_weight_from_f32, say, to_dev_x
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_and_check(w32, x_bits, what):
+    n, k = w32.shape
+    blocks = O.quantize(w32)
+    pw, _ = device_weight_from_f32(w32)
+    say("linear", what)
+    y = q4.linear(to_dev_x(x_bits), pw).cpu().numpy()
+    return assert_within_bound(y, O.linear(x_bits, blocks, n, k), O.error_bound(x_bits, blocks, n, k), what)
+
+
+MS = [1, 2, 3, 4, 5, 16, 17, 31, 32, 33, 64, 100, 129, 300]
+NKS = [(16, 32), (48, 128), (40, 96), (200, 384), (1040, 1280), (96, 3072)]
+
+
+@pytest.mark.parametrize("m", MS)
+@pytest.mark.parametrize("n,k", NKS)
+def test_linear_parity_grid(m, n, k):
+    w = inputs.weights_f32((n, k), seed=21, tags=(n, k))
+    x = inputs.activations_bf16((m, k), seed=21, tags=(m, k))
+    _run_and_check(w, x, f"M={m} N={n} K={k}")
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 16, 32, 64])
+def test_all_codes_eight_give_zero(m):
+    n, k = 64, 512
+    rng = np.random.default_rng(m)
+    d = (rng.standard_normal((n, k // 32)) * 10).astype(np.float16)
+    blocks = O.gguf_encode(d, np.full((n, k), 8, dtype=np.uint8))
+    x = inputs.activations_bf16((m, k), seed=m)
+    pw = device_weight_from_blocks(blocks, n, k)
+    say("all-q8", m)
+    y = q4.linear(to_dev_x(x), pw).cpu().numpy()
+    assert np.all(np.abs(y) <= 1e-6)
+
+
+@pytest.mark.parametrize("m", [1, 2, 5, 32, 33])
+def test_single_nonzero_nibble(m):
+    n, k = 48, 384
+    rng = np.random.default_rng(100 + m)
+    x = inputs.activations_bf16((m, k), seed=100 + m)
+    for trial in range(4):
+        q = np.full((n, k), 8, dtype=np.uint8)
+        rows = rng.integers(0, n, size=3)
+        cols = rng.integers(0, k, size=3)
+        q[rows, cols] = rng.integers(0, 16, size=3)
+        d = (rng.standard_normal((n, k // 32)) * 0.05).astype(np.float16)
+        blocks = O.gguf_encode(d, q)
+        pw = device_weight_from_blocks(blocks, n, k)
+        say("single nibble", m, trial)
+        y = q4.linear(to_dev_x(x), pw).cpu().numpy()
+        assert_within_bound(y, O.linear(x, blocks, n, k), O.error_bound(x, blocks, n, k), f"nibble m={m}")
+
+
+@pytest.mark.parametrize("e", [-24, -10, 0, 7, 15])
+def test_power_of_two_scales_and_wide_activations(e):
+    n, k, m = 32, 256, 3
+    rng = np.random.default_rng(e + 50)
+    q = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
+    sign = np.where(rng.random((n, k // 32)) < 0.5, -1.0, 1.0)
+    d = (sign * 2.0**e).astype(np.float16)
+    blocks = O.gguf_encode(d, q)
+    # activations over many binades (bf16 keeps fp32's exponent range)
+    xf = (rng.standard_normal((m, k)) * np.exp2(rng.integers(-60, 60, size=(m, k)))).astype(np.float32)
+    x = inputs.bf16_bits_from_f32(xf)
+    pw = device_weight_from_blocks(blocks, n, k)
+    say("pow2 scales", e)
+    y = q4.linear(to_dev_x(x), pw).cpu().numpy()
+    assert_within_bound(y, O.linear(x, blocks, n, k), O.error_bound(x, blocks, n, k), f"e={e}")
+
+
+@pytest.mark.parametrize("m", [1, 2, 32, 70])
+def test_reads_no_activation_beyond_k(m):
+    """x sits in a larger buffer whose tail is NaN; padded K must not touch it."""
+    n, k = 32, 96                                     # K pads to 128 inside the layout
+    w = inputs.weights_f32((n, k), seed=5)
+    x = inputs.activations_bf16((m, k), seed=5)
+    blocks = O.quantize(w)
+    pw = device_weight_from_blocks(blocks, n, k)
+    big = torch.full((m * k + 4096,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    xv = big[: m * k].view(m, k)
+    xv.copy_(to_dev_x(x))
+    say("nan tail", m)
+    y = q4.linear(xv, pw).cpu().numpy()
+    assert_within_bound(y, O.linear(x, blocks, n, k), O.error_bound(x, blocks, n, k), "nan tail")
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 17, 32, 40, 300])
+def test_multi_equals_separate_calls_bitwise(m):
+    k = 384
+    ns = (64, 16, 40, 200)
+    ws = [inputs.weights_f32((n, k), seed=9, tags=(i,)) for i, n in enumerate(ns)]
+    pws = [device_weight_from_f32(w)[0] for w in ws]
+    x = to_dev_x(inputs.activations_bf16((m, k), seed=9))
+    say("multi", m)
+    ys = q4.linear_multi(x, pws)
+    for w, pw, y in zip(ws, pws, ys):
+        single = q4.linear(x, pw)
+        assert torch.equal(y, single)
+    xb = inputs.activations_bf16((m, k), seed=9)
+    for w, y in zip(ws, ys):
+        b = O.quantize(w)
+        assert_within_bound(y.cpu().numpy(), O.linear(xb, b, w.shape[0], k), O.error_bound(xb, b, w.shape[0], k))
+
+
+@pytest.mark.parametrize("m", [1, 2, 32, 129])
+def test_bitwise_deterministic(m):
+    n, k = 512, 1024
+    pw, _ = device_weight_from_f32(inputs.weights_f32((n, k), seed=3))
+    x = to_dev_x(inputs.activations_bf16((m, k), seed=3))
+    say("determinism", m)
+    y0 = q4.linear(x, pw)
+    for _ in range(3):
+        assert torch.equal(q4.linear(x, pw), y0)
+
+
+def test_m_zero_is_a_no_op():
+    n, k = 32, 64
+    pw, _ = device_weight_from_f32(inputs.weights_f32((n, k), seed=1))
+    y = torch.full((0, n), 7.0, device=DEV)
+    x = torch.empty((0, k), dtype=torch.bfloat16, device=DEV)
+    q4.linear(x, pw, out=y)
+    sentinel = torch.full((4, n), 7.0, device=DEV)
+    assert q4.lib().q4_0_linear(x.data_ptr(), 0, pw.data.data_ptr(), n, k, sentinel.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    assert torch.all(sentinel == 7.0)
