@@ -133,6 +133,26 @@ typedef struct {
 q4_status q4_0_linear_multi(const void *x_bf16, int64_t M, int64_t K, const q4_0_segment *segs,
                             int nseg, void *stream);
 
+/*
+ * Name of the kernel instantiation q4_0_linear runs for this M and K (the
+ * configuration depends on M and K only, never on N, so a fused launch and
+ * separate launches of its segments run the same arithmetic).  Static string;
+ * "" for an invalid M or K.  For reports that match timings to kernel names.
+ */
+const char *q4_0_linear_kernel(int64_t M, int64_t K);
+
+/*
+ * Measurement hook for benchmarks.  Arms the calling thread's next
+ * q4_0_linear / q4_0_linear_multi launch so that its kernel records
+ * `start_event` when it starts executing and `stop_event` when it finishes
+ * (hipExtLaunchKernelGGL); hipEventElapsedTime on the pair is then that
+ * kernel's own duration, without launch gaps -- the quantity a kernel trace
+ * reports.  Events are hipEvent_t created by the caller; either may be NULL.
+ * One-shot: the arming is consumed by the next launch (or by a validation
+ * failure of that call it is kept).  Not for use under stream capture.
+ */
+q4_status q4_0_time_next_launch(void *start_event, void *stop_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,10 +14,12 @@ from ._binding import (  # noqa: F401
     lib,
     library_path,
     linear,
+    linear_kernel,
     linear_multi,
     pack,
     packed_bytes,
     quantize,
     status_str,
+    time_next_launch,
     unpack,
 )

@@ -21,7 +21,8 @@ Q4_OK = 0
 STATUS_NAMES = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIGN",
                 4: "Q4_ERR_SEGMENTS", 5: "Q4_ERR_HIP"}
 EXPORTS = ("q4_status_str", "q4_0_packed_bytes", "q4_0_quantize", "q4_0_pack", "q4_0_unpack",
-           "q4_0_dequant", "q4_0_linear", "q4_0_linear_multi")
+           "q4_0_dequant", "q4_0_linear", "q4_0_linear_multi", "q4_0_time_next_launch",
+           "q4_0_linear_kernel")
 
 
 class Q4Error(ValueError):
@@ -65,6 +66,10 @@ def lib() -> ctypes.CDLL:
             L.q4_0_linear.restype = i32
             L.q4_0_linear_multi.argtypes = [vp, i64, i64, ctypes.POINTER(Segment), i32, vp]
             L.q4_0_linear_multi.restype = i32
+            L.q4_0_linear_kernel.argtypes = [i64, i64]
+            L.q4_0_linear_kernel.restype = ctypes.c_char_p
+            L.q4_0_time_next_launch.argtypes = [vp, vp]
+            L.q4_0_time_next_launch.restype = i32
             _lib = L
     return _lib
 
@@ -202,3 +207,14 @@ def linear_multi(x: torch.Tensor, weights, outs=None):
         _check(lib().q4_0_linear_multi(x.data_ptr(), m, k, segs, len(weights), _stream(x.device)),
                "q4_0_linear_multi")
     return outs
+
+
+def time_next_launch(start: "torch.cuda.Event", stop: "torch.cuda.Event") -> None:
+    """Arm this thread's next linear launch to record start/stop at its kernel's
+    own start and end (events must already exist: record them once first)."""
+    _check(lib().q4_0_time_next_launch(start.cuda_event, stop.cuda_event), "q4_0_time_next_launch")
+
+
+def linear_kernel(m: int, k: int) -> str:
+    """Name of the kernel q4_0_linear runs for (M, K)."""
+    return lib().q4_0_linear_kernel(int(m), int(k)).decode()

@@ -33,6 +33,9 @@ COMMON_FLAGS = [
     # Packed fp32 VALU ops stay off: every fp32 op is issued one lane value
     # at a time.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the per-block fp32 rescale reads them directly
+    # instead of copying each one out of an AGPR first.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}",
     f"-I{CSRC}",

@@ -119,4 +119,14 @@ q4_status q4_0_linear_multi(const void *x_bf16, int64_t M, int64_t K, const q4_0
     return from_hip(q4::launch_linear(a, as_stream(stream)));
 }
 
+const char *q4_0_linear_kernel(int64_t M, int64_t K) {
+    if (M < 1 || M > kMaxM || !shape_ok(1, K)) return "";
+    return q4::linear_config_name(M, K);
+}
+
+q4_status q4_0_time_next_launch(void *start_event, void *stop_event) {
+    q4::arm_launch_events(reinterpret_cast<hipEvent_t>(start_event), reinterpret_cast<hipEvent_t>(stop_event));
+    return Q4_OK;
+}
+
 }  // extern "C"

@@ -57,4 +57,12 @@ hipError_t launch_dequant(const uint8_t *packed, int64_t N, int64_t K, float *w,
 // filled in by the launcher).
 hipError_t launch_linear(LinearArgs a, hipStream_t s);
 
+// Name of the kernel instantiation launch_linear picks for (M, K); the
+// XLDS flag in it is the choice when x fits in LDS.
+const char *linear_config_name(int64_t M, int64_t K);
+
+// Makes the calling thread's next launch_linear record `start` / `stop` at
+// its kernel's start and end.
+void arm_launch_events(hipEvent_t start, hipEvent_t stop);
+
 }  // namespace q4

@@ -25,6 +25,7 @@
 //                  shared by the WN waves; weights again go HBM -> registers.
 // Neither kernel uses atomics: results are bitwise reproducible.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_fp16.h>
 
 #include "q4_0_internal.h"
@@ -67,6 +68,28 @@ __device__ __forceinline__ bf16x8 decode_piece(uint32_t w) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Split decode: the fp32 (q - 8) / 16 that v_cvt_off_f32_i4 returns has
+// only 3 significant bits, so its low 16 bits are zero and the register is
+// already a bf16 pair (+0, (q - 8) / 16).  Used as an MFMA operand as is, it
+// carries one weight per pair; the even elements of a piece (low nibbles)
+// and the odd ones (high nibbles) then take one MFMA each, against x with
+// its pairs swapped and as stored.  That drops the pack instructions of
+// decode_piece at the price of a second MFMA per block.
+__device__ __forceinline__ bf16x8 decode_even(uint32_t w) {
+    return __builtin_bit_cast(bf16x8, (floatx4){code_of_byte<0>(w), code_of_byte<1>(w),
+                                                code_of_byte<2>(w), code_of_byte<3>(w)});
+}
+__device__ __forceinline__ bf16x8 decode_odd(uint32_t w) {
+    uint32_t h = w >> 4;
+    asm("" : "+v"(h));
+    return __builtin_bit_cast(bf16x8, (floatx4){code_of_byte<0>(h), code_of_byte<1>(h),
+                                                code_of_byte<2>(h), code_of_byte<3>(h)});
+}
+
+__device__ __forceinline__ floatx4 mfma_acc(const bf16x8 &a, const bf16x8 &b, const floatx4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
     return __half2float(__ushort_as_half(static_cast<unsigned short>(bits16)));
 }
@@ -94,19 +117,36 @@ __device__ __forceinline__ int find_segment(const LinearArgs &a, int tile) {
 }
 
 // ------------------------------------------------------------------ skinny
-template <int MROWS, int NT, int WK, int P>
+// x staged in LDS: row m of the (padded) x tile starts at m * row_bytes; rows
+// are padded by 16 bytes so the 16 rows read by one MFMA A fragment fall in
+// different LDS banks.  Two copies: x as stored, then x with the two bf16 of
+// every 32-bit pair swapped (the A operand of the even-element MFMA of the
+// split decode).
+__device__ __forceinline__ int x_row_bytes(int KT) { return KT * kTileK * 2 + 16; }
+
+template <int MROWS, int NT, int WK, int P, bool XLDS, bool SPLIT, int WPE>
 struct SkinnyCfg {
     static constexpr int MT = MROWS > 16 ? 2 : 1;        // 16-row m-tiles
     static constexpr int REGS = MROWS < 4 ? MROWS : 4;   // live accumulator rows per lane
     static constexpr int kThreads = 64 * WK;
 };
 
-template <int MROWS, int NT, int WK, int P>
-__global__ __launch_bounds__(64 * WK) void skinny_kernel(const LinearArgs a) {
-    using C = SkinnyCfg<MROWS, NT, WK, P>;
+// Decode-sized batches.  Every wave owns all M rows, NT weight row-tiles
+// (16 rows each) and the super-tiles kt = wk, wk + WK, ... along K.  All of a
+// wave's weight loads (up to P super-tiles) are issued before anything else,
+// so a launch puts its whole weight stream in flight at once; x is staged
+// once per workgroup (in LDS when XLDS) while those loads are outstanding.
+template <int MROWS, int NT, int WK, int P, bool XLDS, bool SPLIT, int WPE>
+__global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
+void skinny_kernel(const LinearArgs a) {
+    using C = SkinnyCfg<MROWS, NT, WK, P, XLDS, SPLIT, WPE>;
     constexpr int MT = C::MT, REGS = C::REGS;
+    extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
     const int lane = threadIdx.x & 63;
-    const int wk = threadIdx.x >> 6;
+    // wave index as a scalar: every loop bound and branch below is uniform
+    // across the wave, so the compiler emits scalar branches and keeps exact
+    // per-stage load counters (no drain of the prefetch queue)
+    const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nl = lane & 15, g = lane >> 4;
 
     const int s = find_segment(a, blockIdx.x);
@@ -114,38 +154,52 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(const LinearArgs a) {
     const int rt0 = (static_cast<int>(blockIdx.x) - sg.tile_begin) * NT;
     const int KT = a.KT;
     const int nblk = a.K / kQK;
+    const int mrows = a.M < 16 * MT ? a.M : 16 * MT;   // staged x rows
+    const int row_bytes = x_row_bytes(KT);
+    const int nkt = (KT - wk + WK - 1) / WK;            // super-tiles of this wave: wk + j * WK
 
-    struct Stage {
+    // Weight tiles past the segment's end are read from its last tile (their
+    // results are never stored), so loads need no branches.
+    const uint8_t *nib_base[NT];
+    const uint16_t *sc_base[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int rt = rt0 + nt < sg.RT ? rt0 + nt : sg.RT - 1;
+        const int64_t T0 = static_cast<int64_t>(rt) * KT + wk;
+        nib_base[nt] = sg.nib + T0 * kTileNibBytes + lane * 16;
+        sc_base[nt] = sg.scales + T0 * kTileScales + nl * 4;
+    }
+
+    struct WStage {
         u32x4 nib[NT];
         u32x2 sc[NT];
-        u32x4 xa[MT][kTileBlocks];
     };
-
-    auto load = [&](Stage &S, int kt) {
+    auto load_w = [&](WStage &S, int j) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const int rt = rt0 + nt;
-            if (rt < sg.RT) {
-                const int64_t T = static_cast<int64_t>(rt) * KT + kt;
-                S.nib[nt] = *reinterpret_cast<const u32x4 *>(sg.nib + T * kTileNibBytes + lane * 16);
-                S.sc[nt] = *reinterpret_cast<const u32x2 *>(sg.scales + T * kTileScales + nl * 4);
-            } else {
-                S.nib[nt] = (u32x4){0u, 0u, 0u, 0u};
-                S.sc[nt] = (u32x2){0u, 0u};
-            }
+            S.nib[nt] = *reinterpret_cast<const u32x4 *>(nib_base[nt] + static_cast<int64_t>(j) * WK * kTileNibBytes);
+            S.sc[nt] = *reinterpret_cast<const u32x2 *>(sc_base[nt] + static_cast<int64_t>(j) * WK * kTileScales);
         }
+    };
+
+    // A fragment of m-tile mt for block b: x[m][32 b + 8 g .. + 8].  Rows at
+    // or beyond M only feed output rows that are never stored, so they read
+    // row M - 1 (from LDS) or zeros (from global memory).
+    int a_row[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = mt * 16 + nl;
-#pragma unroll
-            for (int i = 0; i < kTileBlocks; ++i) {
-                const int b = kt * kTileBlocks + i;
-                if (m < a.M && b < nblk)
-                    S.xa[mt][i] = *reinterpret_cast<const u32x4 *>(
-                        a.x + static_cast<int64_t>(m) * a.K + b * kQK + g * 8);
-                else
-                    S.xa[mt][i] = (u32x4){0u, 0u, 0u, 0u};
-            }
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + nl;
+        a_row[mt] = XLDS ? (m < mrows ? m : mrows - 1) : m;
+    }
+    auto load_a = [&](int mt, int b, int copy) -> bf16x8 {
+        if constexpr (XLDS) {
+            return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
+                                                  xs + (copy * mrows + a_row[mt]) * row_bytes + (b * kQK + g * 8) * 2));
+        } else {
+            u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+            if (a_row[mt] < a.M && b < nblk)
+                v = *reinterpret_cast<const u32x4 *>(a.x + static_cast<int64_t>(a_row[mt]) * a.K + b * kQK + g * 8);
+            return __builtin_bit_cast(bf16x8, v);
         }
     };
 
@@ -155,43 +209,93 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(const LinearArgs a) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const Stage &S) {
+    auto compute = [&](const WStage &S, int j) {
+        const int kt = wk + j * WK;
 #pragma unroll
         for (int i = 0; i < kTileBlocks; ++i) {
-            bf16x8 A[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) A[mt] = __builtin_bit_cast(bf16x8, S.xa[mt][i]);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const bf16x8 B = decode_piece(piece_of(S.nib[nt], i));
-                const float d = scale_of(S.sc[nt], i);
+            const int b = kt * kTileBlocks + i;
+            if constexpr (XLDS && SPLIT) {
+                bf16x8 Ao[MT], As[MT];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    const floatx4 D = mfma_block(A[mt], B);
+                    Ao[mt] = load_a(mt, b, 0);
+                    As[mt] = load_a(mt, b, 1);
+                }
 #pragma unroll
-                    for (int r = 0; r < REGS; ++r) acc[nt][mt][r] = fmaf(d, D[r], acc[nt][mt][r]);
+                for (int nt = 0; nt < NT; ++nt) {
+                    const uint32_t w = piece_of(S.nib[nt], i);
+                    const bf16x8 Be = decode_even(w), Bo = decode_odd(w);
+                    const float d = scale_of(S.sc[nt], i);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const floatx4 D = mfma_acc(Ao[mt], Bo, mfma_block(As[mt], Be));
+#pragma unroll
+                        for (int r = 0; r < REGS; ++r) acc[nt][mt][r] = fmaf(d, D[r], acc[nt][mt][r]);
+                    }
+                }
+            } else {
+                bf16x8 A[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) A[mt] = load_a(mt, b, 0);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const bf16x8 B = decode_piece(piece_of(S.nib[nt], i));
+                    const float d = scale_of(S.sc[nt], i);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const floatx4 D = mfma_block(A[mt], B);
+#pragma unroll
+                        for (int r = 0; r < REGS; ++r) acc[nt][mt][r] = fmaf(d, D[r], acc[nt][mt][r]);
+                    }
                 }
             }
         }
     };
 
-    Stage st[P];
+    // 1. weight loads for the first P super-tiles of this wave
+    WStage st[P];
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-        const int kt = wk + p * WK;
-        if (kt < KT) load(st[p], kt);
-    }
-    for (int base = wk; base < KT; base += P * WK) {
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            const int kt = base + p * WK;
-            if (kt < KT) {
-                compute(st[p]);
-                const int ktn = kt + P * WK;
-                if (ktn < KT) load(st[p], ktn);
+    for (int p = 0; p < P; ++p)
+        if (p < nkt) load_w(st[p], p);
+    // 2. stage x (zero beyond K) while they are in flight: as stored, and
+    //    with each bf16 pair swapped
+    if constexpr (XLDS) {
+        const int chunks_per_row = KT * (kTileK / 8);          // 16-byte chunks
+        const int total = mrows * chunks_per_row;
+        for (int c = threadIdx.x; c < total; c += C::kThreads) {
+            const int m = c / chunks_per_row, kc = c - m * chunks_per_row;
+            u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+            if (kc * 8 < a.K) v = *reinterpret_cast<const u32x4 *>(a.x + static_cast<int64_t>(m) * a.K + kc * 8);
+            *reinterpret_cast<u32x4 *>(xs + m * row_bytes + kc * 16) = v;
+            if constexpr (SPLIT) {
+                const u32x4 sw = (u32x4){__builtin_amdgcn_alignbit(v.x, v.x, 16), __builtin_amdgcn_alignbit(v.y, v.y, 16),
+                                         __builtin_amdgcn_alignbit(v.z, v.z, 16), __builtin_amdgcn_alignbit(v.w, v.w, 16)};
+                *reinterpret_cast<u32x4 *>(xs + (mrows + m) * row_bytes + kc * 16) = sw;
             }
         }
+        __syncthreads();
     }
+    // 3. steady state: P computes, each followed by the refill of its stage
+    //    P super-tiles ahead; no conditions inside
+    int j = 0;
+    for (; j + 2 * P <= nkt; j += P) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            compute(st[p], j + p);
+            load_w(st[p], j + p + P);
+        }
+    }
+    // 4. drain: at most 2P - 1 super-tiles remain
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        if (j + p < nkt) {
+            compute(st[p], j + p);
+            if (j + p + P < nkt) load_w(st[p], j + p + P);
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+        if (j + P + p < nkt) compute(st[p], j + P + p);
 
     // Sum the WK partial results in wave order through LDS.
     if constexpr (WK > 1) {
@@ -245,14 +349,16 @@ struct GemmCfg {
 // Byte offset of 16-byte chunk c (0..15) of row m in a swizzled A tile.
 __device__ __forceinline__ int a_tile_offset(int m, int c) { return (m * 16 + (c ^ (m & 7))) * 16; }
 
-template <int MT, int NT, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const LinearArgs a) {
+template <int MT, int NT, int WM, int WN, int WPE>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
+void gemm_kernel(const LinearArgs a) {
     using C = GemmCfg<MT, NT, WM, WN>;
     constexpr int BM = C::BM, NPT = C::kAPerThread;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * 256];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: uniform branches
     const int wm = wave / WN, wn = wave % WN;
     const int nl = lane & 15, g = lane >> 4;
 
@@ -271,11 +377,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const LinearArgs a) 
             const int q = tid + C::kThreads * j;
             const int m = q >> 4, c = q & 15;
             const int b = kt * kTileBlocks + (c >> 2);
+            a_regs[j] = (u32x4){0u, 0u, 0u, 0u};
             if (m0 + m < a.M && b < nblk)
                 a_regs[j] = *reinterpret_cast<const u32x4 *>(
                     a.x + static_cast<int64_t>(m0 + m) * a.K + kt * kTileK + c * 8);
-            else
-                a_regs[j] = (u32x4){0u, 0u, 0u, 0u};
         }
     };
     auto store_a = [&](int buf) {
@@ -287,7 +392,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const LinearArgs a) 
         }
     };
 
-    // ---- B: this wave's NT weight tiles, straight into registers
+    // ---- B: this wave's NT weight tiles, straight into registers.  Tiles
+    // past the segment's end read its last tile (never stored).
+    const uint8_t *nib_base[NT];
+    const uint16_t *sc_base[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int rt = rt_base + nt < sg.RT ? rt_base + nt : sg.RT - 1;
+        const int64_t T0 = static_cast<int64_t>(rt) * KT;
+        nib_base[nt] = sg.nib + T0 * kTileNibBytes + lane * 16;
+        sc_base[nt] = sg.scales + T0 * kTileScales + nl * 4;
+    }
     struct BStage {
         u32x4 nib[NT];
         u32x2 sc[NT];
@@ -295,15 +410,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const LinearArgs a) 
     auto load_b = [&](BStage &S, int kt) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const int rt = rt_base + nt;
-            if (rt < sg.RT) {
-                const int64_t T = static_cast<int64_t>(rt) * KT + kt;
-                S.nib[nt] = *reinterpret_cast<const u32x4 *>(sg.nib + T * kTileNibBytes + lane * 16);
-                S.sc[nt] = *reinterpret_cast<const u32x2 *>(sg.scales + T * kTileScales + nl * 4);
-            } else {
-                S.nib[nt] = (u32x4){0u, 0u, 0u, 0u};
-                S.sc[nt] = (u32x2){0u, 0u};
-            }
+            S.nib[nt] = *reinterpret_cast<const u32x4 *>(nib_base[nt] + static_cast<int64_t>(kt) * kTileNibBytes);
+            S.sc[nt] = *reinterpret_cast<const u32x2 *>(sc_base[nt] + static_cast<int64_t>(kt) * kTileScales);
         }
     };
 
@@ -312,6 +420,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const LinearArgs a) 
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (floatx4){0.f, 0.f, 0.f, 0.f};
+
+    int a_off[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) a_off[mt] = ((wm * MT + mt) * 16 + nl) * 256;
 
     auto compute = [&](int buf, const BStage &S) {
         const uint8_t *tile = lds_a[buf];
@@ -322,7 +434,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const LinearArgs a) 
             for (int mt = 0; mt < MT; ++mt) {
                 const int m = (wm * MT + mt) * 16 + nl;
                 A[mt] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4 *>(tile + a_tile_offset(m, 4 * i + g)));
+                    bf16x8, *reinterpret_cast<const u32x4 *>(tile + a_off[mt] + (((4 * i + g) ^ (m & 7)) * 16)));
             }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
@@ -334,6 +446,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const LinearArgs a) 
 #pragma unroll
                     for (int r = 0; r < 4; ++r) acc[mt][nt][r] = fmaf(d, D[r], acc[mt][nt][r]);
                 }
+                // keep one weight tile's MFMAs and rescales together: bounds
+                // the live MFMA results (register pressure -> occupancy)
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
@@ -346,22 +461,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const LinearArgs a) 
     int kt = 0;
     for (;;) {
         // even step: compute kt from buffer 0 / b0, prefetch kt+1 into buffer 1 / b1
-        if (kt + 1 < KT) {
+        const bool more0 = kt + 1 < KT;
+        if (more0) {
             load_a(kt + 1);
             load_b(b1, kt + 1);
         }
         compute(0, b0);
-        if (kt + 1 >= KT) break;
+        if (!more0) break;
         store_a(1);
         __syncthreads();
         ++kt;
         // odd step
-        if (kt + 1 < KT) {
+        const bool more1 = kt + 1 < KT;
+        if (more1) {
             load_a(kt + 1);
             load_b(b0, kt + 1);
         }
         compute(1, b1);
-        if (kt + 1 >= KT) break;
+        if (!more1) break;
         store_a(0);
         __syncthreads();
         ++kt;
@@ -383,20 +500,53 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const LinearArgs a) 
 }
 
 // ---------------------------------------------------------------- launch
+// Events armed by q4_0_time_next_launch for this thread's next linear launch.
+thread_local hipEvent_t t_start_event = nullptr;
+thread_local hipEvent_t t_stop_event = nullptr;
+
+template <typename Kernel>
+hipError_t launch_kernel(Kernel kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
+                         const LinearArgs &a) {
+    if (t_start_event || t_stop_event) {
+        hipEvent_t start = t_start_event, stop = t_stop_event;
+        t_start_event = t_stop_event = nullptr;
+        // records the events at the kernel's own start and end
+        hipExtLaunchKernelGGL(kernel, grid, block, lds, s, start, stop, 0, a);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, a);
+    }
+    return hipGetLastError();
+}
+
 // Tile configurations depend on M only, so a fused multi-segment launch and
 // separate single launches run the same arithmetic in the same order.
-template <int MROWS, int NT, int WK, int P>
+constexpr uint32_t kMaxXLds = 128 * 1024;  // dynamic LDS budget for staged x (both copies)
+
+template <int MROWS, int NT, int WK, int P, bool SPLIT = true, int WPE = 0>
 hipError_t run_skinny(LinearArgs a, hipStream_t s) {
     int tiles = 0;
     for (int i = 0; i < a.nseg; ++i) {
         a.seg[i].tile_begin = tiles;
         tiles += (a.seg[i].RT + NT - 1) / NT;
     }
-    hipLaunchKernelGGL((skinny_kernel<MROWS, NT, WK, P>), dim3(tiles), dim3(64 * WK), 0, s, a);
-    return hipGetLastError();
+    constexpr int MT = MROWS > 16 ? 2 : 1;
+    const int mrows = a.M < 16 * MT ? a.M : 16 * MT;
+    const uint64_t lds = (SPLIT ? 2 : 1) * static_cast<uint64_t>(mrows) * (static_cast<uint64_t>(a.KT) * kTileK * 2 + 16);
+    if (MROWS <= 16 && lds <= kMaxXLds) {
+        auto kernel = skinny_kernel<MROWS, NT, WK, P, true, SPLIT, WPE>;
+        static bool raised = false;   // per instantiation: allow the dynamic LDS size once
+        if (!raised) {
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kMaxXLds);
+            if (e != hipSuccess) return e;
+            raised = true;
+        }
+        return launch_kernel(kernel, dim3(tiles), dim3(64 * WK), static_cast<uint32_t>(lds), s, a);
+    }
+    return launch_kernel(skinny_kernel<MROWS, NT, WK, P, false, false, WPE>, dim3(tiles), dim3(64 * WK), 0, s, a);
 }
 
-template <int MT, int NT, int WM, int WN>
+template <int MT, int NT, int WM, int WN, int WPE = 0>
 hipError_t run_gemm(LinearArgs a, hipStream_t s) {
     using C = GemmCfg<MT, NT, WM, WN>;
     int tiles = 0;
@@ -405,19 +555,57 @@ hipError_t run_gemm(LinearArgs a, hipStream_t s) {
         tiles += (a.seg[i].RT + NT * WN - 1) / (NT * WN);
     }
     const int mtiles = (a.M + C::BM - 1) / C::BM;
-    hipLaunchKernelGGL((gemm_kernel<MT, NT, WM, WN>), dim3(tiles, mtiles), dim3(C::kThreads), 0, s, a);
-    return hipGetLastError();
+    return launch_kernel(gemm_kernel<MT, NT, WM, WN, WPE>, dim3(tiles, mtiles), dim3(C::kThreads), 0, s, a);
 }
 
 }  // namespace
 
+void arm_launch_events(hipEvent_t start, hipEvent_t stop) {
+    t_start_event = start;
+    t_stop_event = stop;
+}
+
+// The dispatch table: kernel configuration by M (and K for M <= 2).  Decode
+// sizes use short K-slices per wave and a shallow prefetch so that many waves
+// stay resident (the launches are latency-bound); long rows split K wider.
+namespace {
+enum class Cfg { M1, M1Long, M2, M2Long, M4, M16, M32, Gemm };
+
+Cfg pick(int64_t M, int64_t K) {
+    const bool long_k = K > 3072;
+    if (M == 1) return long_k ? Cfg::M1Long : Cfg::M1;
+    if (M == 2) return long_k ? Cfg::M2Long : Cfg::M2;
+    if (M <= 4) return Cfg::M4;
+    if (M <= 16) return Cfg::M16;
+    if (M <= 32) return Cfg::M32;
+    return Cfg::Gemm;
+}
+}  // namespace
+
+const char *linear_config_name(int64_t M, int64_t K) {
+    switch (pick(M, K)) {
+        case Cfg::M1: return "skinny_kernel<1, 1, 4, 2, true, false, 6>";
+        case Cfg::M1Long: return "skinny_kernel<1, 1, 8, 3, true, false, 0>";
+        case Cfg::M2: return "skinny_kernel<2, 1, 4, 2, true, false, 6>";
+        case Cfg::M2Long: return "skinny_kernel<2, 1, 8, 3, true, false, 0>";
+        case Cfg::M4: return "skinny_kernel<4, 1, 4, 2, true, false, 0>";
+        case Cfg::M16: return "skinny_kernel<16, 1, 4, 2, true, false, 0>";
+        case Cfg::M32: return "skinny_kernel<32, 4, 4, 2, false, false, 0>";
+        default: return "gemm_kernel<4, 1, 2, 8, 4>";
+    }
+}
+
 hipError_t launch_linear(LinearArgs a, hipStream_t s) {
-    if (a.M == 1) return run_skinny<1, 1, 8, 4>(a, s);
-    if (a.M == 2) return run_skinny<2, 1, 8, 4>(a, s);
-    if (a.M <= 4) return run_skinny<4, 1, 8, 4>(a, s);
-    if (a.M <= 16) return run_skinny<16, 1, 8, 4>(a, s);
-    if (a.M <= 32) return run_skinny<32, 4, 4, 2>(a, s);
-    return run_gemm<4, 4, 2, 2>(a, s);
+    switch (pick(a.M, a.K)) {
+        case Cfg::M1: return run_skinny<1, 1, 4, 2, false, 6>(a, s);
+        case Cfg::M1Long: return run_skinny<1, 1, 8, 3, false, 0>(a, s);
+        case Cfg::M2: return run_skinny<2, 1, 4, 2, false, 6>(a, s);
+        case Cfg::M2Long: return run_skinny<2, 1, 8, 3, false, 0>(a, s);
+        case Cfg::M4: return run_skinny<4, 1, 4, 2, false, 0>(a, s);
+        case Cfg::M16: return run_skinny<16, 1, 4, 2, false, 0>(a, s);
+        case Cfg::M32: return run_skinny<32, 4, 4, 2>(a, s);
+        default: return run_gemm<4, 1, 2, 8, 4>(a, s);
+    }
 }
 
 }  // namespace q4
