@@ -346,8 +346,10 @@ struct GemmCfg {
     static_assert(kAChunks % kThreads == 0, "A tile must split evenly over the threads");
 };
 
-// Byte offset of 16-byte chunk c (0..15) of row m in a swizzled A tile.
-__device__ __forceinline__ int a_tile_offset(int m, int c) { return (m * 16 + (c ^ (m & 7))) * 16; }
+// Byte offset of 16-byte chunk c (0..15) of row m in a swizzled A tile: the
+// chunk index is XORed with the row's low 4 bits, so the 16 rows read by one
+// MFMA A fragment (same chunk) land in 16 different chunk slots.
+__device__ __forceinline__ int a_tile_offset(int m, int c) { return (m * 16 + (c ^ (m & 15))) * 16; }
 
 template <int MT, int NT, int WM, int WN, int WPE>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
@@ -434,7 +436,7 @@ void gemm_kernel(const LinearArgs a) {
             for (int mt = 0; mt < MT; ++mt) {
                 const int m = (wm * MT + mt) * 16 + nl;
                 A[mt] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4 *>(tile + a_off[mt] + (((4 * i + g) ^ (m & 7)) * 16)));
+                    bf16x8, *reinterpret_cast<const u32x4 *>(tile + a_off[mt] + (((4 * i + g) ^ (m & 15)) * 16)));
             }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
@@ -569,7 +571,7 @@ void arm_launch_events(hipEvent_t start, hipEvent_t stop) {
 // sizes use short K-slices per wave and a shallow prefetch so that many waves
 // stay resident (the launches are latency-bound); long rows split K wider.
 namespace {
-enum class Cfg { M1, M1Long, M2, M2Long, M4, M16, M32, Gemm };
+enum class Cfg { M1, M1Long, M2, M2Long, M4, M16, M32, M64, Gemm };
 
 Cfg pick(int64_t M, int64_t K) {
     const bool long_k = K > 3072;
@@ -578,6 +580,7 @@ Cfg pick(int64_t M, int64_t K) {
     if (M <= 4) return Cfg::M4;
     if (M <= 16) return Cfg::M16;
     if (M <= 32) return Cfg::M32;
+    if (M <= 64) return Cfg::M64;
     return Cfg::Gemm;
 }
 }  // namespace
@@ -590,7 +593,8 @@ const char *linear_config_name(int64_t M, int64_t K) {
         case Cfg::M2Long: return "skinny_kernel<2, 1, 8, 3, true, false, 0>";
         case Cfg::M4: return "skinny_kernel<4, 1, 4, 2, true, false, 0>";
         case Cfg::M16: return "skinny_kernel<16, 1, 4, 2, true, false, 0>";
-        case Cfg::M32: return "skinny_kernel<32, 4, 4, 2, false, false, 0>";
+        case Cfg::M32: return "gemm_kernel<2, 1, 1, 8, 0>";
+        case Cfg::M64: return "gemm_kernel<4, 1, 1, 8, 0>";
         default: return "gemm_kernel<4, 1, 2, 8, 4>";
     }
 }
@@ -603,7 +607,8 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
         case Cfg::M2Long: return run_skinny<2, 1, 8, 3, false, 0>(a, s);
         case Cfg::M4: return run_skinny<4, 1, 4, 2, false, 0>(a, s);
         case Cfg::M16: return run_skinny<16, 1, 4, 2, false, 0>(a, s);
-        case Cfg::M32: return run_skinny<32, 4, 4, 2>(a, s);
+        case Cfg::M32: return run_gemm<2, 1, 1, 8, 0>(a, s);
+        case Cfg::M64: return run_gemm<4, 1, 1, 8, 0>(a, s);
         default: return run_gemm<4, 1, 2, 8, 4>(a, s);
     }
 }
