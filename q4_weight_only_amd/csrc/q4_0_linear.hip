@@ -13,17 +13,23 @@
 // dequantization split so that no weight is ever rounded.
 //
 // Kernels.
-//   skinny_kernel  (M <= 32, decode-sized batches): a wave owns all M rows,
+//   skinny_kernel  (M <= 16, decode-sized batches): a wave owns all M rows,
 //                  NT 16-row weight tiles and every WK-th super-tile along K;
 //                  weights go straight from HBM into MFMA B registers (each
 //                  lane's 16-byte load is exactly its B slice for 4 blocks),
-//                  x comes from global memory (L2-resident), and the WK waves
-//                  of a workgroup are summed through LDS in a fixed order.
-//   gemm_kernel    (M > 32, prefill / encoder sizes): a workgroup tile of
-//                  BM x BN outputs; the x tile of each 128-k step is staged in
-//                  LDS (double-buffered, XOR-swizzled 16-byte chunks) and
-//                  shared by the WN waves; weights again go HBM -> registers.
-// Neither kernel uses atomics: results are bitwise reproducible.
+//                  x comes from LDS (staged once) or global memory, and the WK
+//                  waves of a workgroup are summed through LDS in a fixed order.
+//   gemm_kernel    (17 <= M <= 64): a workgroup tile of BM x BN outputs; the x
+//                  tile of each 128-k step is staged in LDS (double-buffered,
+//                  XOR-swizzled 16-byte chunks) and shared by the WN waves;
+//                  weights again go HBM -> registers.
+//   gemm3_kernel   (M > 64, prefill / encoder sizes): the same arithmetic with
+//                  MT x NT register tiles per wave, x staged a quarter per
+//                  block step through bounds-checked buffer loads, and an
+//                  XCD-aware workgroup -> tile order.
+// gemm_kernel and gemm3_kernel add the block results of an output in the same
+// order, so they give bitwise equal results for any tiling.
+// No kernel uses atomics: results are bitwise reproducible.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_fp16.h>
@@ -351,6 +357,12 @@ struct GemmCfg {
 // MFMA A fragment (same chunk) land in 16 different chunk slots.
 __device__ __forceinline__ int a_tile_offset(int m, int c) { return (m * 16 + (c ^ (m & 15))) * 16; }
 
+// Word 3 of a raw buffer resource on gfx9: 32-bit data format, so untyped
+// loads are bounds-checked against the resource's byte size and read zero
+// past it.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kOutOfRange = 0x40000000;   // a byte offset beyond every x resource (at most 2^29 bytes)
+
 template <int MT, int NT, int WM, int WN, int WPE>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
 void gemm_kernel(const LinearArgs a) {
@@ -501,6 +513,197 @@ void gemm_kernel(const LinearArgs a) {
     }
 }
 
+// ------------------------------------------------------------------- gemm3
+// Prefill-sized M with register tiles of MT x NT MFMA tiles per wave.  The
+// x tile of the next 128-k step is staged a quarter per block step (so the
+// staging registers stay few) into the other LDS buffer; the rescale of
+// each group of MFMA results is issued after the next group's MFMAs, so the
+// FMAs never wait on a result still in flight.  Work tiles are mapped to
+// workgroups so that each of the 8 XCDs owns a contiguous range of them, in
+// an order where GM consecutive tiles share one weight tile.
+template <int MT, int NT, int WM, int WN>
+struct Gemm3Cfg {
+    static constexpr int BM = 16 * MT * WM;
+    static constexpr int BN = 16 * NT * WN;
+    static constexpr int kThreads = 64 * WM * WN;
+    static constexpr int kAStep = BM * 16 / kTileBlocks;   // 16-byte x chunks staged per block step
+    // Threads per staged chunk set: all threads, or kAStep of them for a small
+    // tile; the other waves then load and store the same chunks again (the
+    // same bytes to the same place), which keeps the loop free of branches.
+    static constexpr int kStagers = kAStep < kThreads ? kAStep : kThreads;
+    static constexpr int kAPerThread = kAStep / kStagers;
+    static_assert(kAStep % kStagers == 0 && kStagers % 64 == 0, "x staging must split evenly over whole waves");
+};
+
+template <int MT, int NT, int WM, int WN, int WPE, int GM>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
+void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
+    using C = Gemm3Cfg<MT, NT, WM, WN>;
+    constexpr int BM = C::BM, NPT = C::kAPerThread;
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * 256];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int nl = lane & 15, g = lane >> 4;
+
+    // workgroup -> tile: XCD x (dispatch round-robins workgroups over the 8
+    // XCDs) takes the x-th contiguous share of the tile order
+    const int nwg = gridDim.x, bid = blockIdx.x;
+    const int q8 = nwg >> 3, r8 = nwg & 7, xcd = bid & 7, local = bid >> 3;
+    const int t = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + local;
+    const int per_group = GM * ntiles;
+    const int first_m = (t / per_group) * GM;
+    const int gsize = mtiles - first_m < GM ? mtiles - first_m : GM;
+    const int within = t - (t / per_group) * per_group;
+    const int mtile = first_m + within % gsize;
+    const int ntile = within / gsize;
+
+    const int s = find_segment(a, ntile);
+    const Segment sg = a.seg[s];
+    const int rt_base = (ntile - sg.tile_begin) * (NT * WN) + wn * NT;
+    const int m0 = mtile * BM;
+    const int KT = a.KT;
+    const int nblk = a.K / kQK;
+
+    // ---- x staging: part p of a tile is chunks p * kAStep + tid % kStagers + kStagers * j.
+    // Loads go through a buffer resource over this tile's rows, so a chunk
+    // past K gets an offset beyond the resource's size and reads zeros, with
+    // no branch.  Rows past M read row M - 1 (their outputs are never stored).
+    const int rows = a.M - m0 < BM ? a.M - m0 : BM;
+    const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.x + static_cast<int64_t>(m0) * a.K), 0, rows * a.K * 2, kBufferRsrcWord3);
+    int x_off[kTileBlocks][NPT];   // byte offset in the tile's rows at k-step 0
+    int x_kt_end[kTileBlocks][NPT];   // first k-step whose chunk lies past K
+#pragma unroll
+    for (int p = 0; p < kTileBlocks; ++p)
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) {
+            const int qc = p * C::kAStep + tid % C::kStagers + C::kStagers * j;
+            const int m = qc >> 4, c = qc & 15;
+            x_off[p][j] = (m < rows ? m : rows - 1) * a.K * 2 + c * 16;
+            x_kt_end[p][j] = (nblk - (c >> 2) + kTileBlocks - 1) / kTileBlocks;
+        }
+    auto load_part = [&](u32x4 (&R)[NPT], int kt, int part) {
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) {
+            const int off = kt < x_kt_end[part][j] ? x_off[part][j] : kOutOfRange;
+            R[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, off, kt * kTileK * 2, 0));
+        }
+    };
+    auto store_part = [&](const u32x4 (&R)[NPT], int buf, int part) {
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) {
+            const int qc = part * C::kAStep + tid % C::kStagers + C::kStagers * j;
+            const int m = qc >> 4, c = qc & 15;
+            *reinterpret_cast<u32x4 *>(&lds_a[buf][a_tile_offset(m, c)]) = R[j];
+        }
+    };
+
+    // ---- weights: this wave's NT tiles, straight into registers
+    const uint8_t *nib_base[NT];
+    const uint16_t *sc_base[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int rt = rt_base + nt < sg.RT ? rt_base + nt : sg.RT - 1;
+        const int64_t T0 = static_cast<int64_t>(rt) * KT;
+        nib_base[nt] = sg.nib + T0 * kTileNibBytes + lane * 16;
+        sc_base[nt] = sg.scales + T0 * kTileScales + nl * 4;
+    }
+    struct BStage {
+        u32x4 nib[NT];
+        u32x2 sc[NT];
+    };
+    auto load_b = [&](BStage &S, int kt) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            S.nib[nt] = *reinterpret_cast<const u32x4 *>(nib_base[nt] + static_cast<int64_t>(kt) * kTileNibBytes);
+            S.sc[nt] = *reinterpret_cast<const u32x2 *>(sc_base[nt] + static_cast<int64_t>(kt) * kTileScales);
+        }
+    };
+
+    floatx4 acc[MT][NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (floatx4){0.f, 0.f, 0.f, 0.f};
+
+    const int a_row0 = (wm * MT) * 16 + nl;   // LDS row of m-tile 0 for this lane; m-tile mt adds 16 mt
+    auto compute_block = [&](int buf, const BStage &S, int i) {
+        const uint8_t *tile = lds_a[buf];
+        const int sw = ((4 * i + g) ^ nl) * 16;   // swizzled chunk of block i (row & 15 == nl)
+        bf16x8 A[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            A[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(tile + (a_row0 + 16 * mt) * 256 + sw));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const bf16x8 B = decode_piece(piece_of(S.nib[nt], i));
+            const float d = scale_of(S.sc[nt], i);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const floatx4 D = mfma_block(A[mt], B);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[mt][nt][r] = fmaf(d, D[r], acc[mt][nt][r]);
+            }
+        }
+        // one block at a time: bounds the live MFMA results and operands
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    u32x4 R0[NPT], R1[NPT];
+    BStage b0, b1;
+    load_b(b0, 0);
+#pragma unroll
+    for (int p = 0; p < kTileBlocks; ++p) {
+        load_part(R0, 0, p);
+        store_part(R0, 0, p);
+    }
+    __syncthreads();
+
+    // One 128-k step with no branches: the loads for step kt + 1 are clamped
+    // to the last step (the extra loads and stores of the final step go to
+    // the buffer nobody reads any more).
+    auto step = [&](int kt, int cur, BStage &bc, BStage &bn) {
+        const int kn = kt + 1 < KT ? kt + 1 : KT - 1;
+        load_b(bn, kn);
+        load_part(R0, kn, 0);
+        compute_block(cur, bc, 0);
+        load_part(R1, kn, 1);
+        store_part(R0, cur ^ 1, 0);
+        compute_block(cur, bc, 1);
+        load_part(R0, kn, 2);
+        store_part(R1, cur ^ 1, 1);
+        compute_block(cur, bc, 2);
+        load_part(R1, kn, 3);
+        store_part(R0, cur ^ 1, 2);
+        compute_block(cur, bc, 3);
+        store_part(R1, cur ^ 1, 3);
+        __syncthreads();
+    };
+    for (int kt = 0;;) {
+        step(kt, 0, b0, b1);
+        if (++kt == KT) break;
+        step(kt, 1, b1, b0);
+        if (++kt == KT) break;
+    }
+
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int rt = rt_base + nt;
+        const int n = rt * 16 + nl;
+        if (rt >= sg.RT || n >= sg.N) continue;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + (wm * MT + mt) * 16 + 4 * g + r;
+                if (m < a.M) sg.y[static_cast<int64_t>(m) * sg.N + n] = acc[mt][nt][r] * 16.0f;
+            }
+    }
+}
+
 // ---------------------------------------------------------------- launch
 // Events armed by q4_0_time_next_launch for this thread's next linear launch.
 thread_local hipEvent_t t_start_event = nullptr;
@@ -560,6 +763,29 @@ hipError_t run_gemm(LinearArgs a, hipStream_t s) {
     return launch_kernel(gemm_kernel<MT, NT, WM, WN, WPE>, dim3(tiles, mtiles), dim3(C::kThreads), 0, s, a);
 }
 
+template <int MT, int NT, int WM, int WN, int WPE = 0, int GM = 8>
+hipError_t run_gemm3(LinearArgs a, hipStream_t s) {
+    using C = Gemm3Cfg<MT, NT, WM, WN>;
+    int ntiles = 0;
+    for (int i = 0; i < a.nseg; ++i) {
+        a.seg[i].tile_begin = ntiles;
+        ntiles += (a.seg[i].RT + NT * WN - 1) / (NT * WN);
+    }
+    const int mtiles = static_cast<int>((a.M + C::BM - 1) / C::BM);
+    const int64_t total = static_cast<int64_t>(ntiles) * mtiles;
+    if (total > 0x7fffffff) return hipErrorInvalidValue;
+    auto kernel = gemm3_kernel<MT, NT, WM, WN, WPE, GM>;
+    const dim3 grid(static_cast<uint32_t>(total)), block(C::kThreads);
+    if (t_start_event || t_stop_event) {
+        hipEvent_t start = t_start_event, stop = t_stop_event;
+        t_start_event = t_stop_event = nullptr;
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, start, stop, 0, a, mtiles, ntiles);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, 0, s, a, mtiles, ntiles);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 void arm_launch_events(hipEvent_t start, hipEvent_t stop) {
@@ -570,8 +796,10 @@ void arm_launch_events(hipEvent_t start, hipEvent_t stop) {
 // The dispatch table: kernel configuration by M (and K for M <= 2).  Decode
 // sizes use short K-slices per wave and a shallow prefetch so that many waves
 // stay resident (the launches are latency-bound); long rows split K wider.
+// Above 64 rows the GEMM takes 64-row tiles below 2048 rows (more workgroups
+// for the 1.5k-row audio shapes) and 128-row tiles from there on.
 namespace {
-enum class Cfg { M1, M1Long, M2, M2Long, M4, M16, M32, M64, Gemm };
+enum class Cfg { M1, M1Long, M2, M2Long, M4, M16, M32, M64, Gemm64, Gemm128 };
 
 Cfg pick(int64_t M, int64_t K) {
     const bool long_k = K > 3072;
@@ -581,7 +809,7 @@ Cfg pick(int64_t M, int64_t K) {
     if (M <= 16) return Cfg::M16;
     if (M <= 32) return Cfg::M32;
     if (M <= 64) return Cfg::M64;
-    return Cfg::Gemm;
+    return M < 2048 ? Cfg::Gemm64 : Cfg::Gemm128;
 }
 }  // namespace
 
@@ -595,7 +823,8 @@ const char *linear_config_name(int64_t M, int64_t K) {
         case Cfg::M16: return "skinny_kernel<16, 1, 4, 2, true, false, 0>";
         case Cfg::M32: return "gemm_kernel<2, 1, 1, 8, 0>";
         case Cfg::M64: return "gemm_kernel<4, 1, 1, 8, 0>";
-        default: return "gemm_kernel<4, 1, 2, 8, 4>";
+        case Cfg::Gemm64: return "gemm3_kernel<4, 1, 1, 8, 4, 8>";
+        default: return "gemm3_kernel<8, 1, 1, 8, 4, 8>";
     }
 }
 
@@ -609,7 +838,8 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
         case Cfg::M16: return run_skinny<16, 1, 4, 2, false, 0>(a, s);
         case Cfg::M32: return run_gemm<2, 1, 1, 8, 0>(a, s);
         case Cfg::M64: return run_gemm<4, 1, 1, 8, 0>(a, s);
-        default: return run_gemm<4, 1, 2, 8, 4>(a, s);
+        case Cfg::Gemm64: return run_gemm3<4, 1, 1, 8, 4, 8>(a, s);
+        default: return run_gemm3<8, 1, 1, 8, 4, 8>(a, s);
     }
 }
 

@@ -1,6 +1,7 @@
 """Parity of the device linear with the oracle on sizes the oracle finishes in
 seconds: every output element within 1e-3 * sum|x w| + 1e-6, across the
-kernel variants (M = 1, 2, 3-4, 5-16, 17-32, > 32), several tiles in N and K,
+kernel variants (M = 1, 2, 3-4, 5-16, 17-32, 33-64, 65-2047, >= 2048), several
+tiles in N and K,
 ragged edges, structured weights, fused segments and determinism."""
 
 import numpy as np
@@ -25,7 +26,7 @@ def _run_and_check(w32, x_bits, what):
     return assert_within_bound(y, O.linear(x_bits, blocks, n, k), O.error_bound(x_bits, blocks, n, k), what)
 
 
-MS = [1, 2, 3, 4, 5, 16, 17, 31, 32, 33, 64, 100, 129, 300]
+MS = [1, 2, 3, 4, 5, 16, 17, 31, 32, 33, 64, 100, 129, 300, 2100]
 NKS = [(16, 32), (48, 128), (40, 96), (200, 384), (1040, 1280), (96, 3072)]
 
 
