@@ -19,4 +19,8 @@ from .q4_0_oracle import (  # noqa: F401
     packed_bytes,
     padded_dims,
     quantize,
+    silu,
+    swiglu,
+    swiglu_bound,
+    swiglu_rows,
 )

@@ -27,6 +27,11 @@ What the oracle computes, and where each step comes from:
   d = fp16(amax / -8), q = clamp(rint(w / d) + 8, 0, 15) with the division in
   fp32 and rint rounding half to even; a block whose fp16 d is zero stores
   d = +0 and q = 8.
+* The gated MLP step after the fused gate/up projection (the Rust fork's
+  "Architecture Summary" names SwiGLU right after the Q4 matmul; its "TTS"
+  section fuses the gate and up projections).  The pages do not spell SwiGLU
+  out; the reading taken is the usual one for this decoder family:
+  h = silu(x Wg^T) * (x Wu^T) elementwise, silu(t) = t / (1 + e^-t).
 * The packed device layout (the "CDNA4 tiled layout") is restated here from
   its definition in include/q4_0.h so the device repack can be checked byte
   for byte.  It is a permutation of the GGUF bytes, plus zero padding.
@@ -152,6 +157,60 @@ def linear_rows(x_bits: np.ndarray, blocks: np.ndarray, n: int, k: int,
     sub = b[np.asarray(rows)]
     nr = sub.shape[0]
     return linear(x_bits, sub, nr, k), error_bound(x_bits, sub, nr, k)
+
+
+# ------------------------------------------------------------------- SwiGLU
+def silu(t) -> np.ndarray:
+    """silu(t) = t * sigmoid(t) = t / (1 + e^-t) in fp64.
+
+    Evaluated as t / (1 + e^-t) for t >= 0 and t * e^t / (1 + e^t) for t < 0,
+    so that no exponential overflows.
+    """
+    t = np.asarray(t, dtype=np.float64)
+    out = np.empty_like(t)
+    pos = t >= 0
+    out[pos] = t[pos] / (1.0 + np.exp(-t[pos]))
+    e = np.exp(t[~pos])
+    out[~pos] = t[~pos] * e / (1.0 + e)
+    return out
+
+
+SILU_SLOPE_MAX = 1.1   # sup |silu'(t)| = 1.0998... (at t near 2.4)
+
+
+def swiglu(x_bits: np.ndarray, gate_blocks: np.ndarray, up_blocks: np.ndarray,
+           n: int, k: int) -> np.ndarray:
+    """h[m, j] = silu(g[m, j]) * u[m, j], g = x Wg^T, u = x Wu^T, in fp64."""
+    g = linear(x_bits, gate_blocks, n, k)
+    u = linear(x_bits, up_blocks, n, k)
+    return silu(g) * u
+
+
+def swiglu_bound(x_bits: np.ndarray, gate_blocks: np.ndarray, up_blocks: np.ndarray,
+                 n: int, k: int) -> np.ndarray:
+    """Tolerance on h when the device's g~ and u~ each meet the linear bound.
+
+    With |g~ - g| <= bg and |u~ - u| <= bu (bg, bu from error_bound):
+      |silu(g~) u~ - silu(g) u| <= |silu(g~) - silu(g)| |u~| + |silu(g)| |u~ - u|
+                                <= 1.1 bg (|u| + bu) + |silu(g)| bu,
+    since |silu'| <= 1.1 everywhere.  A relative 1e-5 of |h| covers the fp32
+    evaluation of the exponential, the division and the product.
+    """
+    g = linear(x_bits, gate_blocks, n, k)
+    u = linear(x_bits, up_blocks, n, k)
+    bg = error_bound(x_bits, gate_blocks, n, k)
+    bu = error_bound(x_bits, up_blocks, n, k)
+    sg = silu(g)
+    return SILU_SLOPE_MAX * bg * (np.abs(u) + bu) + np.abs(sg) * bu + 1e-5 * np.abs(sg * u)
+
+
+def swiglu_rows(x_bits: np.ndarray, gate_blocks: np.ndarray, up_blocks: np.ndarray,
+                n: int, k: int, rows: np.ndarray):
+    """(h, bound) restricted to the output columns `rows` (sampled checks)."""
+    gb = np.ascontiguousarray(gate_blocks, dtype=np.uint8).reshape(n, k // QK, BLOCK_BYTES)[np.asarray(rows)]
+    ub = np.ascontiguousarray(up_blocks, dtype=np.uint8).reshape(n, k // QK, BLOCK_BYTES)[np.asarray(rows)]
+    nr = gb.shape[0]
+    return swiglu(x_bits, gb, ub, nr, k), swiglu_bound(x_bits, gb, ub, nr, k)
 
 
 # ------------------------------------------------------------------ quantizer
