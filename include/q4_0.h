@@ -134,6 +134,30 @@ q4_status q4_0_linear_multi(const void *x_bf16, int64_t M, int64_t K, const q4_0
                             int nseg, void *stream);
 
 /*
+ * Fused gate/up projection with the SwiGLU epilogue (the gated MLP of the
+ * decoder: the Rust fork's "Architecture Summary" puts SwiGLU right after
+ * the Q4 matmul, and its "TTS" section fuses the gate and up projections):
+ *
+ *   h[m, n] = silu(g[m, n]) * u[m, n],   g = x Wg^T,  u = x Wu^T,
+ *   silu(t) = t / (1 + e^-t),
+ *
+ * with gate_packed (Wg) and up_packed (Wu) packed [N, K] matrices of the same
+ * shape and h fp32 [M, N] (device, row-major).  One launch; g and u never
+ * reach memory, so the output is half the bytes of a gate/up
+ * q4_0_linear_multi.  g and u are computed exactly as q4_0_linear computes
+ * them, and silu and the product in fp32, so h is within
+ * 1.1 bg (|u| + bu) + |silu(g)| bu + 1e-5 |h| of the exact value, where bg
+ * and bu are the q4_0_linear bounds of g and u.  Arguments are validated as
+ * for q4_0_linear (both weight pointers); deterministic.
+ */
+q4_status q4_0_linear_swiglu(const void *x_bf16, int64_t M, int64_t K, const void *gate_packed,
+                             const void *up_packed, int64_t N, float *h, void *stream);
+
+/* Name of the kernel instantiation q4_0_linear_swiglu runs for M and K
+ * (static string; "" for an invalid M or K). */
+const char *q4_0_linear_swiglu_kernel(int64_t M, int64_t K);
+
+/*
  * Name of the kernel instantiation q4_0_linear runs for this M and K (the
  * configuration depends on M and K only, never on N, so a fused launch and
  * separate launches of its segments run the same arithmetic).  Static string;
@@ -143,7 +167,7 @@ const char *q4_0_linear_kernel(int64_t M, int64_t K);
 
 /*
  * Measurement hook for benchmarks.  Arms the calling thread's next
- * q4_0_linear / q4_0_linear_multi launch so that its kernel records
+ * q4_0_linear / q4_0_linear_multi / q4_0_linear_swiglu launch so that its kernel records
  * `start_event` when it starts executing and `stop_event` when it finishes
  * (hipExtLaunchKernelGGL); hipEventElapsedTime on the pair is then that
  * kernel's own duration, without launch gaps -- the quantity a kernel trace

@@ -16,6 +16,8 @@ from ._binding import (  # noqa: F401
     linear,
     linear_kernel,
     linear_multi,
+    linear_swiglu,
+    linear_swiglu_kernel,
     pack,
     packed_bytes,
     quantize,

@@ -22,7 +22,7 @@ STATUS_NAMES = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIG
                 4: "Q4_ERR_SEGMENTS", 5: "Q4_ERR_HIP"}
 EXPORTS = ("q4_status_str", "q4_0_packed_bytes", "q4_0_quantize", "q4_0_pack", "q4_0_unpack",
            "q4_0_dequant", "q4_0_linear", "q4_0_linear_multi", "q4_0_time_next_launch",
-           "q4_0_linear_kernel")
+           "q4_0_linear_kernel", "q4_0_linear_swiglu", "q4_0_linear_swiglu_kernel")
 
 
 class Q4Error(ValueError):
@@ -68,6 +68,10 @@ def lib() -> ctypes.CDLL:
             L.q4_0_linear_multi.restype = i32
             L.q4_0_linear_kernel.argtypes = [i64, i64]
             L.q4_0_linear_kernel.restype = ctypes.c_char_p
+            L.q4_0_linear_swiglu.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
+            L.q4_0_linear_swiglu.restype = i32
+            L.q4_0_linear_swiglu_kernel.argtypes = [i64, i64]
+            L.q4_0_linear_swiglu_kernel.restype = ctypes.c_char_p
             L.q4_0_time_next_launch.argtypes = [vp, vp]
             L.q4_0_time_next_launch.restype = i32
             _lib = L
@@ -209,6 +213,26 @@ def linear_multi(x: torch.Tensor, weights, outs=None):
     return outs
 
 
+def linear_swiglu(x: torch.Tensor, gate: PackedWeight, up: PackedWeight,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """h [M, N] fp32 = silu(x Wg^T) * (x Wu^T) in one launch (gate and up [N, K])."""
+    _dev(x, "x", torch.bfloat16)
+    if gate.n != up.n or gate.k != up.k:
+        raise ValueError("gate and up must have the same shape")
+    if x.dim() != 2 or x.shape[1] != gate.k:
+        raise ValueError(f"x must be [M, {gate.k}]")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, gate.n), dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    if tuple(out.shape) != (m, gate.n):
+        raise ValueError("out has the wrong shape")
+    with torch.cuda.device(x.device):
+        _check(lib().q4_0_linear_swiglu(x.data_ptr(), m, gate.k, gate.data.data_ptr(), up.data.data_ptr(),
+                                        gate.n, out.data_ptr(), _stream(x.device)), "q4_0_linear_swiglu")
+    return out
+
+
 def time_next_launch(start: "torch.cuda.Event", stop: "torch.cuda.Event") -> None:
     """Arm this thread's next linear launch to record start/stop at its kernel's
     own start and end (events must already exist: record them once first)."""
@@ -218,3 +242,8 @@ def time_next_launch(start: "torch.cuda.Event", stop: "torch.cuda.Event") -> Non
 def linear_kernel(m: int, k: int) -> str:
     """Name of the kernel q4_0_linear runs for (M, K)."""
     return lib().q4_0_linear_kernel(int(m), int(k)).decode()
+
+
+def linear_swiglu_kernel(m: int, k: int) -> str:
+    """Name of the kernel q4_0_linear_swiglu runs for (M, K)."""
+    return lib().q4_0_linear_swiglu_kernel(int(m), int(k)).decode()

@@ -119,6 +119,30 @@ q4_status q4_0_linear_multi(const void *x_bf16, int64_t M, int64_t K, const q4_0
     return from_hip(q4::launch_linear(a, as_stream(stream)));
 }
 
+q4_status q4_0_linear_swiglu(const void *x_bf16, int64_t M, int64_t K, const void *gate_packed,
+                             const void *up_packed, int64_t N, float *h, void *stream) {
+    if (M < 0 || M > kMaxM || !shape_ok(N, K)) return Q4_ERR_SHAPE;
+    if (M == 0) return Q4_OK;
+    if (!x_bf16 || !gate_packed || !up_packed || !h) return Q4_ERR_NULL;
+    if (!aligned16(x_bf16) || !aligned16(gate_packed) || !aligned16(up_packed) || !aligned16(h))
+        return Q4_ERR_ALIGN;
+    q4::LinearArgs a;
+    a.x = static_cast<const uint16_t *>(x_bf16);
+    a.M = static_cast<int32_t>(M);
+    a.K = static_cast<int32_t>(K);
+    a.KT = static_cast<int32_t>(q4::round_up(K, q4::kTileK) / q4::kTileK);
+    a.nseg = 2;
+    for (int i = 0; i < q4::kMaxSegments; ++i) a.seg[i] = q4::Segment{};
+    a.seg[0] = make_segment(gate_packed, N, K, h);
+    a.seg[1] = make_segment(up_packed, N, K, nullptr);
+    return from_hip(q4::launch_linear_glu(a, as_stream(stream)));
+}
+
+const char *q4_0_linear_swiglu_kernel(int64_t M, int64_t K) {
+    if (M < 1 || M > kMaxM || !shape_ok(1, K)) return "";
+    return q4::linear_glu_config_name(M, K);
+}
+
 const char *q4_0_linear_kernel(int64_t M, int64_t K) {
     if (M < 1 || M > kMaxM || !shape_ok(1, K)) return "";
     return q4::linear_config_name(M, K);

@@ -61,6 +61,11 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s);
 // XLDS flag in it is the choice when x fits in LDS.
 const char *linear_config_name(int64_t M, int64_t K);
 
+// The gated launch: segment 0 is gate (its y receives silu(gate) * up),
+// segment 1 is up, of the same shape; tile_begin is filled in here too.
+hipError_t launch_linear_glu(LinearArgs a, hipStream_t s);
+const char *linear_glu_config_name(int64_t M, int64_t K);
+
 // Makes the calling thread's next launch_linear record `start` / `stop` at
 // its kernel's start and end.
 void arm_launch_events(hipEvent_t start, hipEvent_t stop);

@@ -113,6 +113,10 @@ __device__ __forceinline__ floatx4 mfma_block(const bf16x8 &a, const bf16x8 &b) 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, (floatx4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 }
 
+// silu(g) = g / (1 + e^-g) in fp32 (expf overflows to +inf for g below
+// about -88, which gives -0: the true value is below 1e-36 there).
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
 // Segment lookup: the segments' work tiles are laid end to end.
 __device__ __forceinline__ int find_segment(const LinearArgs &a, int tile) {
     int s = 0;
@@ -142,7 +146,12 @@ struct SkinnyCfg {
 // wave's weight loads (up to P super-tiles) are issued before anything else,
 // so a launch puts its whole weight stream in flight at once; x is staged
 // once per workgroup (in LDS when XLDS) while those loads are outstanding.
-template <int MROWS, int NT, int WK, int P, bool XLDS, bool SPLIT, int WPE>
+//
+// GLU: the launch has two segments of the same shape, gate (seg 0, whose y
+// receives the result) and up (seg 1); the first NT / 2 tiles of a wave are
+// gate rows and the last NT / 2 the same rows of up, and the epilogue stores
+// silu(gate) * up.
+template <int MROWS, int NT, int WK, int P, bool XLDS, bool SPLIT, int WPE, bool GLU>
 __global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
 void skinny_kernel(const LinearArgs a) {
     using C = SkinnyCfg<MROWS, NT, WK, P, XLDS, SPLIT, WPE>;
@@ -155,9 +164,12 @@ void skinny_kernel(const LinearArgs a) {
     const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nl = lane & 15, g = lane >> 4;
 
-    const int s = find_segment(a, blockIdx.x);
+    static_assert(!GLU || NT % 2 == 0, "a gated launch pairs gate and up tiles");
+    constexpr int NTO = GLU ? NT / 2 : NT;             // output row tiles per workgroup
+    constexpr int kUp = GLU ? NTO : 0;                 // tile index offset of the up rows
+    const int s = GLU ? 0 : find_segment(a, blockIdx.x);
     const Segment sg = a.seg[s];
-    const int rt0 = (static_cast<int>(blockIdx.x) - sg.tile_begin) * NT;
+    const int rt0 = (static_cast<int>(blockIdx.x) - sg.tile_begin) * NTO;
     const int KT = a.KT;
     const int nblk = a.K / kQK;
     const int mrows = a.M < 16 * MT ? a.M : 16 * MT;   // staged x rows
@@ -170,10 +182,12 @@ void skinny_kernel(const LinearArgs a) {
     const uint16_t *sc_base[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const int rt = rt0 + nt < sg.RT ? rt0 + nt : sg.RT - 1;
+        const Segment &src = (GLU && nt >= NTO) ? a.seg[1] : sg;
+        const int rtn = rt0 + nt % NTO;
+        const int rt = rtn < src.RT ? rtn : src.RT - 1;
         const int64_t T0 = static_cast<int64_t>(rt) * KT + wk;
-        nib_base[nt] = sg.nib + T0 * kTileNibBytes + lane * 16;
-        sc_base[nt] = sg.scales + T0 * kTileScales + nl * 4;
+        nib_base[nt] = src.nib + T0 * kTileNibBytes + lane * 16;
+        sc_base[nt] = src.scales + T0 * kTileScales + nl * 4;
     }
 
     struct WStage {
@@ -327,7 +341,7 @@ void skinny_kernel(const LinearArgs a) {
     }
 
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < NTO; ++nt) {
         const int rt = rt0 + nt;
         const int n = rt * 16 + nl;
         if (rt >= sg.RT || n >= sg.N) continue;
@@ -336,7 +350,9 @@ void skinny_kernel(const LinearArgs a) {
 #pragma unroll
             for (int r = 0; r < REGS; ++r) {
                 const int m = mt * 16 + 4 * g + r;
-                if (m < a.M) sg.y[static_cast<int64_t>(m) * sg.N + n] = acc[nt][mt][r] * 16.0f;
+                if (m >= a.M) continue;
+                const float v = acc[nt][mt][r] * 16.0f;
+                sg.y[static_cast<int64_t>(m) * sg.N + n] = GLU ? silu_f32(v) * (acc[nt + kUp][mt][r] * 16.0f) : v;
             }
     }
 }
@@ -535,7 +551,9 @@ struct Gemm3Cfg {
     static_assert(kAStep % kStagers == 0 && kStagers % 64 == 0, "x staging must split evenly over whole waves");
 };
 
-template <int MT, int NT, int WM, int WN, int WPE, int GM>
+// GLU: gate / up pairing as in skinny_kernel (the first NT / 2 tiles of a
+// wave are gate rows, the last NT / 2 the same rows of up).
+template <int MT, int NT, int WM, int WN, int WPE, int GM, bool GLU>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
 void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
     using C = Gemm3Cfg<MT, NT, WM, WN>;
@@ -560,9 +578,12 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
     const int mtile = first_m + within % gsize;
     const int ntile = within / gsize;
 
-    const int s = find_segment(a, ntile);
+    static_assert(!GLU || NT % 2 == 0, "a gated launch pairs gate and up tiles");
+    constexpr int NTO = GLU ? NT / 2 : NT;   // output row tiles per wave
+    constexpr int kUp = GLU ? NTO : 0;       // tile index offset of the up rows
+    const int s = GLU ? 0 : find_segment(a, ntile);
     const Segment sg = a.seg[s];
-    const int rt_base = (ntile - sg.tile_begin) * (NT * WN) + wn * NT;
+    const int rt_base = (ntile - sg.tile_begin) * (NTO * WN) + wn * NTO;
     const int m0 = mtile * BM;
     const int KT = a.KT;
     const int nblk = a.K / kQK;
@@ -606,10 +627,12 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
     const uint16_t *sc_base[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const int rt = rt_base + nt < sg.RT ? rt_base + nt : sg.RT - 1;
+        const Segment &src = (GLU && nt >= NTO) ? a.seg[1] : sg;
+        const int rtn = rt_base + nt % NTO;
+        const int rt = rtn < src.RT ? rtn : src.RT - 1;
         const int64_t T0 = static_cast<int64_t>(rt) * KT;
-        nib_base[nt] = sg.nib + T0 * kTileNibBytes + lane * 16;
-        sc_base[nt] = sg.scales + T0 * kTileScales + nl * 4;
+        nib_base[nt] = src.nib + T0 * kTileNibBytes + lane * 16;
+        sc_base[nt] = src.scales + T0 * kTileScales + nl * 4;
     }
     struct BStage {
         u32x4 nib[NT];
@@ -690,7 +713,7 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
     }
 
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < NTO; ++nt) {
         const int rt = rt_base + nt;
         const int n = rt * 16 + nl;
         if (rt >= sg.RT || n >= sg.N) continue;
@@ -699,7 +722,9 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + (wm * MT + mt) * 16 + 4 * g + r;
-                if (m < a.M) sg.y[static_cast<int64_t>(m) * sg.N + n] = acc[mt][nt][r] * 16.0f;
+                if (m >= a.M) continue;
+                const float v = acc[mt][nt][r] * 16.0f;
+                sg.y[static_cast<int64_t>(m) * sg.N + n] = GLU ? silu_f32(v) * (acc[mt][nt + kUp][r] * 16.0f) : v;
             }
     }
 }
@@ -727,18 +752,32 @@ hipError_t launch_kernel(Kernel kernel, dim3 grid, dim3 block, uint32_t lds, hip
 // separate single launches run the same arithmetic in the same order.
 constexpr uint32_t kMaxXLds = 128 * 1024;  // dynamic LDS budget for staged x (both copies)
 
-template <int MROWS, int NT, int WK, int P, bool SPLIT = true, int WPE = 0>
-hipError_t run_skinny(LinearArgs a, hipStream_t s) {
+// Work tiles of a launch: the segments' tiles laid end to end, each tile
+// covering `rows_per_tile` 16-row tiles; a gated launch tiles the gate rows
+// only (the up rows ride along in the same workgroups).
+template <bool GLU>
+int assign_tiles(LinearArgs &a, int rows_per_tile) {
+    if (GLU) {
+        a.seg[0].tile_begin = 0;
+        a.seg[1].tile_begin = 0;
+        return (a.seg[0].RT + rows_per_tile - 1) / rows_per_tile;
+    }
     int tiles = 0;
     for (int i = 0; i < a.nseg; ++i) {
         a.seg[i].tile_begin = tiles;
-        tiles += (a.seg[i].RT + NT - 1) / NT;
+        tiles += (a.seg[i].RT + rows_per_tile - 1) / rows_per_tile;
     }
+    return tiles;
+}
+
+template <int MROWS, int NT, int WK, int P, bool SPLIT = true, int WPE = 0, bool GLU = false>
+hipError_t run_skinny(LinearArgs a, hipStream_t s) {
+    const int tiles = assign_tiles<GLU>(a, GLU ? NT / 2 : NT);
     constexpr int MT = MROWS > 16 ? 2 : 1;
     const int mrows = a.M < 16 * MT ? a.M : 16 * MT;
     const uint64_t lds = (SPLIT ? 2 : 1) * static_cast<uint64_t>(mrows) * (static_cast<uint64_t>(a.KT) * kTileK * 2 + 16);
     if (MROWS <= 16 && lds <= kMaxXLds) {
-        auto kernel = skinny_kernel<MROWS, NT, WK, P, true, SPLIT, WPE>;
+        auto kernel = skinny_kernel<MROWS, NT, WK, P, true, SPLIT, WPE, GLU>;
         static bool raised = false;   // per instantiation: allow the dynamic LDS size once
         if (!raised) {
             const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
@@ -748,33 +787,25 @@ hipError_t run_skinny(LinearArgs a, hipStream_t s) {
         }
         return launch_kernel(kernel, dim3(tiles), dim3(64 * WK), static_cast<uint32_t>(lds), s, a);
     }
-    return launch_kernel(skinny_kernel<MROWS, NT, WK, P, false, false, WPE>, dim3(tiles), dim3(64 * WK), 0, s, a);
+    return launch_kernel(skinny_kernel<MROWS, NT, WK, P, false, false, WPE, GLU>, dim3(tiles), dim3(64 * WK), 0, s, a);
 }
 
 template <int MT, int NT, int WM, int WN, int WPE = 0>
 hipError_t run_gemm(LinearArgs a, hipStream_t s) {
     using C = GemmCfg<MT, NT, WM, WN>;
-    int tiles = 0;
-    for (int i = 0; i < a.nseg; ++i) {
-        a.seg[i].tile_begin = tiles;
-        tiles += (a.seg[i].RT + NT * WN - 1) / (NT * WN);
-    }
+    const int tiles = assign_tiles<false>(a, NT * WN);
     const int mtiles = (a.M + C::BM - 1) / C::BM;
     return launch_kernel(gemm_kernel<MT, NT, WM, WN, WPE>, dim3(tiles, mtiles), dim3(C::kThreads), 0, s, a);
 }
 
-template <int MT, int NT, int WM, int WN, int WPE = 0, int GM = 8>
+template <int MT, int NT, int WM, int WN, int WPE = 0, int GM = 8, bool GLU = false>
 hipError_t run_gemm3(LinearArgs a, hipStream_t s) {
     using C = Gemm3Cfg<MT, NT, WM, WN>;
-    int ntiles = 0;
-    for (int i = 0; i < a.nseg; ++i) {
-        a.seg[i].tile_begin = ntiles;
-        ntiles += (a.seg[i].RT + NT * WN - 1) / (NT * WN);
-    }
+    const int ntiles = assign_tiles<GLU>(a, (GLU ? NT / 2 : NT) * WN);
     const int mtiles = static_cast<int>((a.M + C::BM - 1) / C::BM);
     const int64_t total = static_cast<int64_t>(ntiles) * mtiles;
     if (total > 0x7fffffff) return hipErrorInvalidValue;
-    auto kernel = gemm3_kernel<MT, NT, WM, WN, WPE, GM>;
+    auto kernel = gemm3_kernel<MT, NT, WM, WN, WPE, GM, GLU>;
     const dim3 grid(static_cast<uint32_t>(total)), block(C::kThreads);
     if (t_start_event || t_stop_event) {
         hipEvent_t start = t_start_event, stop = t_stop_event;
@@ -815,16 +846,16 @@ Cfg pick(int64_t M, int64_t K) {
 
 const char *linear_config_name(int64_t M, int64_t K) {
     switch (pick(M, K)) {
-        case Cfg::M1: return "skinny_kernel<1, 1, 4, 2, true, false, 6>";
-        case Cfg::M1Long: return "skinny_kernel<1, 1, 8, 3, true, false, 0>";
-        case Cfg::M2: return "skinny_kernel<2, 1, 4, 2, true, false, 6>";
-        case Cfg::M2Long: return "skinny_kernel<2, 1, 8, 3, true, false, 0>";
-        case Cfg::M4: return "skinny_kernel<4, 1, 4, 2, true, false, 0>";
-        case Cfg::M16: return "skinny_kernel<16, 1, 4, 2, true, false, 0>";
+        case Cfg::M1: return "skinny_kernel<1, 1, 4, 2, true, false, 6, false>";
+        case Cfg::M1Long: return "skinny_kernel<1, 1, 8, 3, true, false, 0, false>";
+        case Cfg::M2: return "skinny_kernel<2, 1, 4, 2, true, false, 6, false>";
+        case Cfg::M2Long: return "skinny_kernel<2, 1, 8, 3, true, false, 0, false>";
+        case Cfg::M4: return "skinny_kernel<4, 1, 4, 2, true, false, 0, false>";
+        case Cfg::M16: return "skinny_kernel<16, 1, 4, 2, true, false, 0, false>";
         case Cfg::M32: return "gemm_kernel<2, 1, 1, 8, 0>";
         case Cfg::M64: return "gemm_kernel<4, 1, 1, 8, 0>";
-        case Cfg::Gemm64: return "gemm3_kernel<4, 1, 1, 8, 4, 8>";
-        default: return "gemm3_kernel<8, 1, 1, 8, 4, 8>";
+        case Cfg::Gemm64: return "gemm3_kernel<4, 1, 1, 8, 4, 8, false>";
+        default: return "gemm3_kernel<8, 1, 1, 8, 4, 8, false>";
     }
 }
 
@@ -840,6 +871,39 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
         case Cfg::M64: return run_gemm<4, 1, 1, 8, 0>(a, s);
         case Cfg::Gemm64: return run_gemm3<4, 1, 1, 8, 4, 8>(a, s);
         default: return run_gemm3<8, 1, 1, 8, 4, 8>(a, s);
+    }
+}
+
+// The gated (SwiGLU) launch: every wave carries a gate tile and the matching
+// up tile, so each configuration is the plain one with NT doubled; above 16
+// rows the gemm3 kernel serves every M.
+const char *linear_glu_config_name(int64_t M, int64_t K) {
+    switch (pick(M, K)) {
+        case Cfg::M1: return "skinny_kernel<1, 2, 4, 2, true, false, 0, true>";
+        case Cfg::M1Long: return "skinny_kernel<1, 2, 8, 3, true, false, 0, true>";
+        case Cfg::M2: return "skinny_kernel<2, 2, 4, 2, true, false, 4, true>";
+        case Cfg::M2Long: return "skinny_kernel<2, 2, 8, 3, true, false, 0, true>";
+        case Cfg::M4: return "skinny_kernel<4, 2, 4, 2, true, false, 0, true>";
+        case Cfg::M16: return "skinny_kernel<16, 2, 4, 2, true, false, 0, true>";
+        case Cfg::M32: return "gemm3_kernel<2, 2, 1, 8, 0, 8, true>";
+        case Cfg::M64: return "gemm3_kernel<4, 2, 1, 8, 0, 8, true>";
+        case Cfg::Gemm64: return "gemm3_kernel<4, 2, 1, 8, 4, 8, true>";
+        default: return "gemm3_kernel<8, 2, 1, 8, 2, 8, true>";
+    }
+}
+
+hipError_t launch_linear_glu(LinearArgs a, hipStream_t s) {
+    switch (pick(a.M, a.K)) {
+        case Cfg::M1: return run_skinny<1, 2, 4, 2, false, 0, true>(a, s);
+        case Cfg::M1Long: return run_skinny<1, 2, 8, 3, false, 0, true>(a, s);
+        case Cfg::M2: return run_skinny<2, 2, 4, 2, false, 4, true>(a, s);
+        case Cfg::M2Long: return run_skinny<2, 2, 8, 3, false, 0, true>(a, s);
+        case Cfg::M4: return run_skinny<4, 2, 4, 2, false, 0, true>(a, s);
+        case Cfg::M16: return run_skinny<16, 2, 4, 2, false, 0, true>(a, s);
+        case Cfg::M32: return run_gemm3<2, 2, 1, 8, 0, 8, true>(a, s);
+        case Cfg::M64: return run_gemm3<4, 2, 1, 8, 0, 8, true>(a, s);
+        case Cfg::Gemm64: return run_gemm3<4, 2, 1, 8, 4, 8, true>(a, s);
+        default: return run_gemm3<8, 2, 1, 8, 2, 8, true>(a, s);
     }
 }
 
