@@ -18,6 +18,9 @@ Printed (one JSON line):
               steps (q4_0_time_next_launch; an eager pass over the same K steps)
   prefill     M=2048 through the four decoder shapes: TFLOP/s (2*M*N*K / time)
               and the GEMM kernel's roofline against 2.5 PFLOP/s bf16
+  swiglu      the fused gate/up + SwiGLU launch (q4_0_linear_swiglu) next to
+              the unfused gate/up launch it replaces, at M = 1, 2 and 2048
+              (kernel-own times over the 26 layers' gate/up weights)
   cpu_baseline  the CPU oracle (dequantize + fp64 matmul) on a bounded sample
               of the same step, on the host cores
 """
@@ -56,6 +59,7 @@ def parse_args():
     p.add_argument("--layers", type=int, default=26, help="decoder layers in a step (26 = the full workload)")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-swiglu", action="store_true", help="skip the fused gate/up + SwiGLU timings")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 256 MiB device copy (reference kernel for PMC byte counters)")
@@ -200,6 +204,59 @@ def time_kernels(runner, steps, dev):
     for i, a, b in pairs:
         per_item[i].append(a.elapsed_time(b) / 1e3)
     return per_item
+
+
+def time_swiglu(prepared, ms, reps, dev):
+    """Kernel-own times of the fused gate/up + SwiGLU launch next to the
+    unfused gate/up launch it replaces, over the decode workload's gate/up
+    weights (one per layer, rotated so the weights stream from HBM)."""
+    import numpy as np
+    import torch
+
+    import q4_weight_only_amd as q4
+
+    gate_up = [(s, pws) for s, pws, _ in prepared if s.name.endswith(".gate_up")]
+    spec0 = gate_up[0][0]
+    n, k = spec0.Ns[0], spec0.K
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for m in ms:
+        xb = spec0.activations(m)
+        x = torch.from_numpy(xb.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+        h = torch.empty((m, n), dtype=torch.float32, device=dev)
+        ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for _ in range(2)]
+        pairs = {"fused": [], "unfused": []}
+        for r in range(reps + 1):
+            for _, pws in gate_up:
+                for kind in ("fused", "unfused"):
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    b.record(stream)
+                    q4.time_next_launch(a, b)
+                    if kind == "fused":
+                        q4.linear_swiglu(x, pws[0], pws[1], h)
+                    else:
+                        q4.linear_multi(x, pws, ys)
+                    if r > 0:              # the first round warms up
+                        pairs[kind].append((a, b))
+        torch.cuda.synchronize(dev)
+        t = {kind: float(np.mean([a.elapsed_time(b) / 1e3 for a, b in v])) for kind, v in pairs.items()}
+        wbytes = spec0.weight_bytes()
+        fused_bytes = wbytes + m * k * 2 + m * n * 4
+        unfused_bytes = wbytes + m * k * 2 + 2 * m * n * 4
+        fl = 2 * m * (2 * n) * k
+        out[f"M={m}"] = {
+            "kernel": q4.linear_swiglu_kernel(m, k),
+            "fused_us": round(t["fused"] * 1e6, 2),
+            "unfused_us": round(t["unfused"] * 1e6, 2),
+            "fused_GBs": round(fused_bytes / t["fused"] / 1e9, 1),
+            "unfused_GBs": round(unfused_bytes / t["unfused"] / 1e9, 1),
+            "fused_TFLOPs": round(fl / t["fused"] / 1e12, 2),
+            "unfused_TFLOPs": round(fl / t["unfused"] / 1e12, 2),
+            "launches": len(pairs["fused"]),
+        }
+    return out
 
 
 def kernel_source_digest():
@@ -392,6 +449,15 @@ def main():
             },
         }
         log(f"prefill: {tflops:.1f} TFLOP/s (kernel {pach:.1f})")
+
+    # ---- NEXT-2: fused gate/up + SwiGLU against the unfused gate/up launch
+    if not args.no_swiglu:
+        out["swiglu"] = {
+            "workload": "decoder gate/up 3072->2x9216 (one weight pair per layer, rotated), "
+                        "h = silu(x Wg^T) * (x Wu^T) fp32",
+            **time_swiglu(prepared, (1, 2, 2048), 3 if args.layers >= 8 else 6, dev),
+        }
+        log(f"swiglu: {out['swiglu']}")
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)

@@ -134,11 +134,12 @@ __device__ __forceinline__ int find_segment(const LinearArgs &a, int tile) {
 // split decode).
 __device__ __forceinline__ int x_row_bytes(int KT) { return KT * kTileK * 2 + 16; }
 
-template <int MROWS, int NT, int WK, int P, bool XLDS, bool SPLIT, int WPE>
+template <int MROWS, int NT, int WK, int P, bool XLDS, bool SPLIT, int WPE, bool GLU>
 struct SkinnyCfg {
     static constexpr int MT = MROWS > 16 ? 2 : 1;        // 16-row m-tiles
     static constexpr int REGS = MROWS < 4 ? MROWS : 4;   // live accumulator rows per lane
-    static constexpr int kThreads = 64 * WK;
+    static constexpr int kWaves = GLU ? 2 * WK : WK;     // waves per workgroup
+    static constexpr int kThreads = 64 * kWaves;
 };
 
 // Decode-sized batches.  Every wave owns all M rows, NT weight row-tiles
@@ -148,28 +149,29 @@ struct SkinnyCfg {
 // once per workgroup (in LDS when XLDS) while those loads are outstanding.
 //
 // GLU: the launch has two segments of the same shape, gate (seg 0, whose y
-// receives the result) and up (seg 1); the first NT / 2 tiles of a wave are
-// gate rows and the last NT / 2 the same rows of up, and the epilogue stores
-// silu(gate) * up.
+// receives the result) and up (seg 1).  A workgroup then has 2 WK waves: the
+// first WK run the gate rows, the last WK the same rows of up, each exactly
+// as a plain launch would; the reduction through LDS sums both in the same
+// wave order and the epilogue stores silu(gate) * up.
 template <int MROWS, int NT, int WK, int P, bool XLDS, bool SPLIT, int WPE, bool GLU>
-__global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
+__global__ __launch_bounds__(64 * WK * (GLU ? 2 : 1)) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
 void skinny_kernel(const LinearArgs a) {
-    using C = SkinnyCfg<MROWS, NT, WK, P, XLDS, SPLIT, WPE>;
+    using C = SkinnyCfg<MROWS, NT, WK, P, XLDS, SPLIT, WPE, GLU>;
     constexpr int MT = C::MT, REGS = C::REGS;
     extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
     const int lane = threadIdx.x & 63;
     // wave index as a scalar: every loop bound and branch below is uniform
     // across the wave, so the compiler emits scalar branches and keeps exact
     // per-stage load counters (no drain of the prefetch queue)
-    const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wk = GLU ? wave % WK : wave;             // K-slice of this wave
+    const bool up_wave = GLU && wave >= WK;            // runs the up rows
     const int nl = lane & 15, g = lane >> 4;
 
-    static_assert(!GLU || NT % 2 == 0, "a gated launch pairs gate and up tiles");
-    constexpr int NTO = GLU ? NT / 2 : NT;             // output row tiles per workgroup
-    constexpr int kUp = GLU ? NTO : 0;                 // tile index offset of the up rows
     const int s = GLU ? 0 : find_segment(a, blockIdx.x);
     const Segment sg = a.seg[s];
-    const int rt0 = (static_cast<int>(blockIdx.x) - sg.tile_begin) * NTO;
+    const Segment &src = up_wave ? a.seg[1] : sg;      // the matrix this wave streams
+    const int rt0 = (static_cast<int>(blockIdx.x) - sg.tile_begin) * NT;
     const int KT = a.KT;
     const int nblk = a.K / kQK;
     const int mrows = a.M < 16 * MT ? a.M : 16 * MT;   // staged x rows
@@ -182,9 +184,7 @@ void skinny_kernel(const LinearArgs a) {
     const uint16_t *sc_base[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const Segment &src = (GLU && nt >= NTO) ? a.seg[1] : sg;
-        const int rtn = rt0 + nt % NTO;
-        const int rt = rtn < src.RT ? rtn : src.RT - 1;
+        const int rt = rt0 + nt < src.RT ? rt0 + nt : src.RT - 1;
         const int64_t T0 = static_cast<int64_t>(rt) * KT + wk;
         nib_base[nt] = src.nib + T0 * kTileNibBytes + lane * 16;
         sc_base[nt] = src.scales + T0 * kTileScales + nl * 4;
@@ -317,19 +317,21 @@ void skinny_kernel(const LinearArgs a) {
     for (int p = 0; p < P; ++p)
         if (j + P + p < nkt) compute(st[p], j + P + p);
 
-    // Sum the WK partial results in wave order through LDS.
-    if constexpr (WK > 1) {
-        __shared__ float red[WK - 1][NT][MT][REGS][64];
-        if (wk > 0) {
+    // Sum the WK partial results in wave order through LDS (gate and up
+    // separately in a gated launch: waves 1 .. WK-1, then WK .. 2WK-1).
+    floatx4 up[NT][MT];
+    if constexpr (C::kWaves > 1) {
+        __shared__ float red[C::kWaves - 1][NT][MT][REGS][64];
+        if (wave > 0) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int r = 0; r < REGS; ++r) red[wk - 1][nt][mt][r][lane] = acc[nt][mt][r];
+                    for (int r = 0; r < REGS; ++r) red[wave - 1][nt][mt][r][lane] = acc[nt][mt][r];
         }
         __syncthreads();
-        if (wk != 0) return;
+        if (wave != 0) return;
 #pragma unroll
         for (int w = 0; w < WK - 1; ++w)
 #pragma unroll
@@ -338,10 +340,22 @@ void skinny_kernel(const LinearArgs a) {
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int r = 0; r < REGS; ++r) acc[nt][mt][r] += red[w][nt][mt][r][lane];
+        if constexpr (GLU) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < REGS; ++r) {
+                        up[nt][mt][r] = red[WK - 1][nt][mt][r][lane];
+#pragma unroll
+                        for (int w = WK; w < 2 * WK - 1; ++w) up[nt][mt][r] += red[w][nt][mt][r][lane];
+                    }
+        }
     }
 
 #pragma unroll
-    for (int nt = 0; nt < NTO; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
         const int rt = rt0 + nt;
         const int n = rt * 16 + nl;
         if (rt >= sg.RT || n >= sg.N) continue;
@@ -352,7 +366,7 @@ void skinny_kernel(const LinearArgs a) {
                 const int m = mt * 16 + 4 * g + r;
                 if (m >= a.M) continue;
                 const float v = acc[nt][mt][r] * 16.0f;
-                sg.y[static_cast<int64_t>(m) * sg.N + n] = GLU ? silu_f32(v) * (acc[nt + kUp][mt][r] * 16.0f) : v;
+                sg.y[static_cast<int64_t>(m) * sg.N + n] = GLU ? silu_f32(v) * (up[nt][mt][r] * 16.0f) : v;
             }
     }
 }
@@ -551,8 +565,10 @@ struct Gemm3Cfg {
     static_assert(kAStep % kStagers == 0 && kStagers % 64 == 0, "x staging must split evenly over whole waves");
 };
 
-// GLU: gate / up pairing as in skinny_kernel (the first NT / 2 tiles of a
-// wave are gate rows, the last NT / 2 the same rows of up).
+// GLU: gate / up as in skinny_kernel: the first WN / 2 waves of a workgroup
+// row run gate rows, the last WN / 2 the same rows of up, each exactly as a
+// plain launch would; the up waves hand their results to the gate waves
+// through LDS for the silu(gate) * up epilogue.
 template <int MT, int NT, int WM, int WN, int WPE, int GM, bool GLU>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
 void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
@@ -578,12 +594,14 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
     const int mtile = first_m + within % gsize;
     const int ntile = within / gsize;
 
-    static_assert(!GLU || NT % 2 == 0, "a gated launch pairs gate and up tiles");
-    constexpr int NTO = GLU ? NT / 2 : NT;   // output row tiles per wave
-    constexpr int kUp = GLU ? NTO : 0;       // tile index offset of the up rows
+    static_assert(!GLU || (WN % 2 == 0 && (WN / 2) * NT <= 8), "gate / up waves and their LDS hand-off");
+    constexpr int WNO = GLU ? WN / 2 : WN;   // waves per workgroup row with distinct output rows
+    const bool up_wave = GLU && wn >= WNO;
+    const int wno = GLU ? wn % WNO : wn;
     const int s = GLU ? 0 : find_segment(a, ntile);
     const Segment sg = a.seg[s];
-    const int rt_base = (ntile - sg.tile_begin) * (NTO * WN) + wn * NTO;
+    const Segment &src = up_wave ? a.seg[1] : sg;   // the matrix this wave streams
+    const int rt_base = (ntile - sg.tile_begin) * (NT * WNO) + wno * NT;
     const int m0 = mtile * BM;
     const int KT = a.KT;
     const int nblk = a.K / kQK;
@@ -627,9 +645,7 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
     const uint16_t *sc_base[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const Segment &src = (GLU && nt >= NTO) ? a.seg[1] : sg;
-        const int rtn = rt_base + nt % NTO;
-        const int rt = rtn < src.RT ? rtn : src.RT - 1;
+        const int rt = rt_base + nt < src.RT ? rt_base + nt : src.RT - 1;
         const int64_t T0 = static_cast<int64_t>(rt) * KT;
         nib_base[nt] = src.nib + T0 * kTileNibBytes + lane * 16;
         sc_base[nt] = src.scales + T0 * kTileScales + nl * 4;
@@ -712,8 +728,24 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
         if (++kt == KT) break;
     }
 
+    // gated: the up waves leave their results in LDS (the x buffers are free
+    // once the last step's barrier has passed) for the matching gate wave
+    float *xch = reinterpret_cast<float *>(&lds_a[0][0]) + (wm * WNO + wno) * (MT * NT * 4 * 64);
+    if constexpr (GLU) {
+        if (up_wave) {
 #pragma unroll
-    for (int nt = 0; nt < NTO; ++nt) {
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) xch[((mt * NT + nt) * 4 + r) * 64 + lane] = acc[mt][nt][r];
+        }
+        __syncthreads();
+        if (up_wave) return;
+    }
+
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
         const int rt = rt_base + nt;
         const int n = rt * 16 + nl;
         if (rt >= sg.RT || n >= sg.N) continue;
@@ -724,7 +756,8 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
                 const int m = m0 + (wm * MT + mt) * 16 + 4 * g + r;
                 if (m >= a.M) continue;
                 const float v = acc[mt][nt][r] * 16.0f;
-                sg.y[static_cast<int64_t>(m) * sg.N + n] = GLU ? silu_f32(v) * (acc[mt][nt + kUp][r] * 16.0f) : v;
+                sg.y[static_cast<int64_t>(m) * sg.N + n] =
+                    GLU ? silu_f32(v) * (xch[((mt * NT + nt) * 4 + r) * 64 + lane] * 16.0f) : v;
             }
     }
 }
@@ -772,7 +805,8 @@ int assign_tiles(LinearArgs &a, int rows_per_tile) {
 
 template <int MROWS, int NT, int WK, int P, bool SPLIT = true, int WPE = 0, bool GLU = false>
 hipError_t run_skinny(LinearArgs a, hipStream_t s) {
-    const int tiles = assign_tiles<GLU>(a, GLU ? NT / 2 : NT);
+    const int tiles = assign_tiles<GLU>(a, NT);
+    constexpr int kThreads = 64 * WK * (GLU ? 2 : 1);
     constexpr int MT = MROWS > 16 ? 2 : 1;
     const int mrows = a.M < 16 * MT ? a.M : 16 * MT;
     const uint64_t lds = (SPLIT ? 2 : 1) * static_cast<uint64_t>(mrows) * (static_cast<uint64_t>(a.KT) * kTileK * 2 + 16);
@@ -785,9 +819,9 @@ hipError_t run_skinny(LinearArgs a, hipStream_t s) {
             if (e != hipSuccess) return e;
             raised = true;
         }
-        return launch_kernel(kernel, dim3(tiles), dim3(64 * WK), static_cast<uint32_t>(lds), s, a);
+        return launch_kernel(kernel, dim3(tiles), dim3(kThreads), static_cast<uint32_t>(lds), s, a);
     }
-    return launch_kernel(skinny_kernel<MROWS, NT, WK, P, false, false, WPE, GLU>, dim3(tiles), dim3(64 * WK), 0, s, a);
+    return launch_kernel(skinny_kernel<MROWS, NT, WK, P, false, false, WPE, GLU>, dim3(tiles), dim3(kThreads), 0, s, a);
 }
 
 template <int MT, int NT, int WM, int WN, int WPE = 0>
@@ -801,7 +835,7 @@ hipError_t run_gemm(LinearArgs a, hipStream_t s) {
 template <int MT, int NT, int WM, int WN, int WPE = 0, int GM = 8, bool GLU = false>
 hipError_t run_gemm3(LinearArgs a, hipStream_t s) {
     using C = Gemm3Cfg<MT, NT, WM, WN>;
-    const int ntiles = assign_tiles<GLU>(a, (GLU ? NT / 2 : NT) * WN);
+    const int ntiles = assign_tiles<GLU>(a, NT * (GLU ? WN / 2 : WN));
     const int mtiles = static_cast<int>((a.M + C::BM - 1) / C::BM);
     const int64_t total = static_cast<int64_t>(ntiles) * mtiles;
     if (total > 0x7fffffff) return hipErrorInvalidValue;
@@ -874,36 +908,36 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
     }
 }
 
-// The gated (SwiGLU) launch: every wave carries a gate tile and the matching
-// up tile, so each configuration is the plain one with NT doubled; above 16
-// rows the gemm3 kernel serves every M.
+// The gated (SwiGLU) launch: the plain configurations with the gate and up
+// rows of a tile on separate waves (skinny: 2 WK waves; gemm3: WN / 2 gate
+// waves and WN / 2 up waves), so every wave runs the plain arithmetic.
 const char *linear_glu_config_name(int64_t M, int64_t K) {
     switch (pick(M, K)) {
-        case Cfg::M1: return "skinny_kernel<1, 2, 4, 2, true, false, 0, true>";
-        case Cfg::M1Long: return "skinny_kernel<1, 2, 8, 3, true, false, 0, true>";
-        case Cfg::M2: return "skinny_kernel<2, 2, 4, 2, true, false, 4, true>";
-        case Cfg::M2Long: return "skinny_kernel<2, 2, 8, 3, true, false, 0, true>";
-        case Cfg::M4: return "skinny_kernel<4, 2, 4, 2, true, false, 0, true>";
-        case Cfg::M16: return "skinny_kernel<16, 2, 4, 2, true, false, 0, true>";
-        case Cfg::M32: return "gemm3_kernel<2, 2, 1, 8, 0, 8, true>";
-        case Cfg::M64: return "gemm3_kernel<4, 2, 1, 8, 0, 8, true>";
-        case Cfg::Gemm64: return "gemm3_kernel<4, 2, 1, 8, 4, 8, true>";
-        default: return "gemm3_kernel<8, 2, 1, 8, 2, 8, true>";
+        case Cfg::M1: return "skinny_kernel<1, 1, 4, 2, true, false, 6, true>";
+        case Cfg::M1Long: return "skinny_kernel<1, 1, 8, 3, true, false, 0, true>";
+        case Cfg::M2: return "skinny_kernel<2, 1, 4, 2, true, false, 6, true>";
+        case Cfg::M2Long: return "skinny_kernel<2, 1, 8, 3, true, false, 0, true>";
+        case Cfg::M4: return "skinny_kernel<4, 1, 4, 2, true, false, 0, true>";
+        case Cfg::M16: return "skinny_kernel<16, 1, 4, 2, true, false, 0, true>";
+        case Cfg::M32: return "gemm3_kernel<2, 1, 1, 8, 0, 8, true>";
+        case Cfg::M64: return "gemm3_kernel<4, 1, 1, 8, 0, 8, true>";
+        case Cfg::Gemm64: return "gemm3_kernel<4, 1, 1, 8, 4, 8, true>";
+        default: return "gemm3_kernel<8, 1, 1, 8, 4, 8, true>";
     }
 }
 
 hipError_t launch_linear_glu(LinearArgs a, hipStream_t s) {
     switch (pick(a.M, a.K)) {
-        case Cfg::M1: return run_skinny<1, 2, 4, 2, false, 0, true>(a, s);
-        case Cfg::M1Long: return run_skinny<1, 2, 8, 3, false, 0, true>(a, s);
-        case Cfg::M2: return run_skinny<2, 2, 4, 2, false, 4, true>(a, s);
-        case Cfg::M2Long: return run_skinny<2, 2, 8, 3, false, 0, true>(a, s);
-        case Cfg::M4: return run_skinny<4, 2, 4, 2, false, 0, true>(a, s);
-        case Cfg::M16: return run_skinny<16, 2, 4, 2, false, 0, true>(a, s);
-        case Cfg::M32: return run_gemm3<2, 2, 1, 8, 0, 8, true>(a, s);
-        case Cfg::M64: return run_gemm3<4, 2, 1, 8, 0, 8, true>(a, s);
-        case Cfg::Gemm64: return run_gemm3<4, 2, 1, 8, 4, 8, true>(a, s);
-        default: return run_gemm3<8, 2, 1, 8, 2, 8, true>(a, s);
+        case Cfg::M1: return run_skinny<1, 1, 4, 2, false, 6, true>(a, s);
+        case Cfg::M1Long: return run_skinny<1, 1, 8, 3, false, 0, true>(a, s);
+        case Cfg::M2: return run_skinny<2, 1, 4, 2, false, 6, true>(a, s);
+        case Cfg::M2Long: return run_skinny<2, 1, 8, 3, false, 0, true>(a, s);
+        case Cfg::M4: return run_skinny<4, 1, 4, 2, false, 0, true>(a, s);
+        case Cfg::M16: return run_skinny<16, 1, 4, 2, false, 0, true>(a, s);
+        case Cfg::M32: return run_gemm3<2, 1, 1, 8, 0, 8, true>(a, s);
+        case Cfg::M64: return run_gemm3<4, 1, 1, 8, 0, 8, true>(a, s);
+        case Cfg::Gemm64: return run_gemm3<4, 1, 1, 8, 4, 8, true>(a, s);
+        default: return run_gemm3<8, 1, 1, 8, 4, 8, true>(a, s);
     }
 }
 
