@@ -9,6 +9,7 @@ from .q4_0_oracle import (  # noqa: F401
     QK,
     bf16_bits_to_f64,
     dequantize,
+    embed,
     error_bound,
     gguf_bytes,
     gguf_decode,

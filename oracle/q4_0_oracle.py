@@ -32,6 +32,12 @@ What the oracle computes, and where each step comes from:
   section fuses the gate and up projections).  The pages do not spell SwiGLU
   out; the reading taken is the usual one for this decoder family:
   h = silu(x Wg^T) * (x Wu^T) elementwise, silu(t) = t / (1 + e^-t).
+* The Q4 embedding lookup: the 131072 x 3072 Q4 table stays on the GPU and
+  token rows are looked up from it (hakusoku, "線形演算・埋め込み"; Rust fork,
+  the browser constraints list: Q4 embeddings on the GPU with row lookups).
+  A lookup returns the dequantized rows w[id, :] = (q - 8) * d, exact in
+  fp32; an id outside [0, N) gives a row of NaN (a reading: the pages say
+  nothing about bad ids, and NaN cannot be mistaken for a real row).
 * The packed device layout (the "CDNA4 tiled layout") is restated here from
   its definition in include/q4_0.h so the device repack can be checked byte
   for byte.  It is a permutation of the GGUF bytes, plus zero padding.
@@ -211,6 +217,19 @@ def swiglu_rows(x_bits: np.ndarray, gate_blocks: np.ndarray, up_blocks: np.ndarr
     ub = np.ascontiguousarray(up_blocks, dtype=np.uint8).reshape(n, k // QK, BLOCK_BYTES)[np.asarray(rows)]
     nr = gb.shape[0]
     return swiglu(x_bits, gb, ub, nr, k), swiglu_bound(x_bits, gb, ub, nr, k)
+
+
+# ----------------------------------------------------------------- embedding
+def embed(blocks: np.ndarray, n: int, k: int, ids) -> np.ndarray:
+    """Rows ids[t] of the dequantized table (fp32, exact); NaN rows for ids
+    outside [0, n)."""
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(n, k // QK, BLOCK_BYTES)
+    ok = (ids >= 0) & (ids < n)
+    out = np.full((ids.size, k), np.nan, dtype=np.float32)
+    if ok.any():
+        out[ok] = dequantize(b[ids[ok]], int(ok.sum()), k)
+    return out
 
 
 # ------------------------------------------------------------------ quantizer

@@ -406,3 +406,33 @@ def test_planted_quantizer_mistakes_are_caught():
     tie = np.zeros((8, 256), dtype=np.float32)
     tie[:, 0], tie[:, 1] = -2.0, 0.625
     assert not np.array_equal(half_up(tie), O.quantize(tie))
+
+
+# ---------------------------------------------------------------- embedding
+def test_embed_rows_by_hand():
+    """Three-row table with hand-built blocks: each looked-up row is (q-8)*d of
+    that row, in the requested order, duplicates repeated, bad ids NaN."""
+    k = 64
+    rows = []
+    for r, d in enumerate((0.5, -2.0, 0.125)):
+        q = [(r * 5 + e) % 16 for e in range(k)]
+        rows.append(np.concatenate([_block(d, q[:32]), _block(d * 3, q[32:])]))
+    table = np.stack(rows)
+    got = O.embed(table, 3, k, [2, 0, 2, -1, 3, 1])
+    assert got.shape == (6, k) and got.dtype == np.float32
+    for t, r in enumerate([2, 0, 2, None, None, 1]):
+        if r is None:
+            assert np.all(np.isnan(got[t]))
+            continue
+        d = (0.5, -2.0, 0.125)[r]
+        want = [((r * 5 + e) % 16 - 8) * (d if e < 32 else d * 3) for e in range(k)]
+        assert got[t].tolist() == want
+
+
+def test_embed_matches_full_dequant():
+    w = inputs.weights_f32((40, 96), seed=9, tags=(9,))
+    blocks = O.quantize(w)
+    ids = np.array([39, 0, 17, 17, 5])
+    full = O.dequantize(blocks, 40, 96)
+    assert np.array_equal(O.embed(blocks, 40, 96, ids), full[ids])
+    assert O.embed(blocks, 40, 96, []).shape == (0, 96)
