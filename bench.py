@@ -21,6 +21,8 @@ Printed (one JSON line):
   swiglu      the fused gate/up + SwiGLU launch (q4_0_linear_swiglu) next to
               the unfused gate/up launch it replaces, at M = 1, 2 and 2048
               (kernel-own times over the 26 layers' gate/up weights)
+  embed       Q4 embedding lookups (q4_0_embed) of 32, 2048 and 16384 random ids
+              from the 131072 x 3072 table: time per launch and GB/s moved
   cpu_baseline  the CPU oracle (dequantize + fp64 matmul) on a bounded sample
               of the same step, on the host cores
 """
@@ -60,6 +62,7 @@ def parse_args():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-swiglu", action="store_true", help="skip the fused gate/up + SwiGLU timings")
+    p.add_argument("--no-embed", action="store_true", help="skip the Q4 embedding lookup timings")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 256 MiB device copy (reference kernel for PMC byte counters)")
@@ -256,6 +259,44 @@ def time_swiglu(prepared, ms, reps, dev):
             "unfused_TFLOPs": round(fl / t["unfused"] / 1e12, 2),
             "launches": len(pairs["fused"]),
         }
+    return out
+
+
+def time_embed(pw, counts, reps, dev):
+    """Q4 embedding lookups from the packed table: `reps` launches captured in
+    one HIP graph, replayed and timed with HIP events (so host launch cost
+    does not count), for each batch size."""
+    import numpy as np
+    import torch
+
+    import q4_weight_only_amd as q4
+
+    rng = np.random.default_rng(7)
+    out = {}
+    stream = torch.cuda.Stream(dev)
+    for count in counts:
+        ids = torch.from_numpy(rng.integers(0, pw.n, count).astype(np.int32)).to(dev)
+        res = torch.empty((count, pw.k), dtype=torch.float32, device=dev)
+        stream.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(stream):
+            q4.embed(pw, ids, res)
+        torch.cuda.synchronize(dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(reps):
+                q4.embed(pw, ids, res)
+        with torch.cuda.stream(stream):
+            graph.replay()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            graph.replay()
+            b.record(stream)
+        b.synchronize()
+        del graph
+        t = a.elapsed_time(b) / 1e3 / reps
+        moved = count * (pw.k // 32 * 18 + pw.k * 4 + 4)     # table rows read + fp32 rows written + ids
+        out[f"ids={count}"] = {"us": round(t * 1e6, 2), "GBs": round(moved / t / 1e9, 1), "bytes": moved}
     return out
 
 
@@ -458,6 +499,18 @@ def main():
             **time_swiglu(prepared, (1, 2, 2048), 3 if args.layers >= 8 else 6, dev),
         }
         log(f"swiglu: {out['swiglu']}")
+
+    # ---- NEXT-3: Q4 embedding lookup from the LM head's table
+    if not args.no_embed:
+        _, lm = inputs.workload(3)
+        lm_spec = lm[0][0]
+        (_, lm_pws, _), = build_device_specs([lm_spec], (), dev)
+        out["embed"] = {
+            "table": f"{lm_spec.Ns[0]}x{lm_spec.K} Q4_0 (the LM head weights), fp32 rows out, random ids",
+            **time_embed(lm_pws[0], (32, 2048, 16384), 50, dev),
+        }
+        log(f"embed: {out['embed']}")
+        del lm_pws
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)

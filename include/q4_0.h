@@ -108,6 +108,19 @@ q4_status q4_0_unpack(const void *packed, int64_t N, int64_t K, void *gguf_block
 q4_status q4_0_dequant(const void *packed, int64_t N, int64_t K, float *w, void *stream);
 
 /*
+ * Q4 embedding lookup (the Q4 table stays on the GPU and token rows are
+ * looked up from it: hakusoku, "線形演算・埋め込み"; Rust fork, the browser
+ * constraints list).  out[t, :] (fp32, device, [n_ids, K] row-major) = row
+ * ids[t] of the packed table [N, K] dequantized, w = (q - 8) * d, exact (the
+ * same values q4_0_dequant gives for that row).  ids: device int32[n_ids].
+ * An id outside [0, N) yields a row of NaN (nothing is read for it).  The
+ * table can be the one a linear uses (a tied LM head).  Sizes as for the
+ * other calls, 0 <= n_ids <= 2^24; n_ids == 0 is a no-op.
+ */
+q4_status q4_0_embed(const void *packed, int64_t N, int64_t K, const int32_t *ids, int64_t n_ids,
+                     float *out, void *stream);
+
+/*
  * y[M, N] (fp32, device) = x[M, K] (bf16, device) times W^T, W packed.
  * Accuracy: every product (q - 8) * x is formed exactly and scaled by d in
  * fp32; y is within 1e-3 * sum_k |x_k * w_k| + 1e-6 of the exact result for

@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     PackedWeight,
     Q4Error,
     dequant,
+    embed,
     gguf_bytes,
     lib,
     library_path,

@@ -22,7 +22,7 @@ STATUS_NAMES = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIG
                 4: "Q4_ERR_SEGMENTS", 5: "Q4_ERR_HIP"}
 EXPORTS = ("q4_status_str", "q4_0_packed_bytes", "q4_0_quantize", "q4_0_pack", "q4_0_unpack",
            "q4_0_dequant", "q4_0_linear", "q4_0_linear_multi", "q4_0_time_next_launch",
-           "q4_0_linear_kernel", "q4_0_linear_swiglu", "q4_0_linear_swiglu_kernel")
+           "q4_0_linear_kernel", "q4_0_linear_swiglu", "q4_0_linear_swiglu_kernel", "q4_0_embed")
 
 
 class Q4Error(ValueError):
@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
                 fn = getattr(L, name)
                 fn.argtypes = [vp, i64, i64, vp, vp]
                 fn.restype = i32
+            L.q4_0_embed.argtypes = [vp, i64, i64, vp, i64, vp, vp]
+            L.q4_0_embed.restype = i32
             L.q4_0_linear.argtypes = [vp, i64, vp, i64, i64, vp, vp]
             L.q4_0_linear.restype = i32
             L.q4_0_linear_multi.argtypes = [vp, i64, i64, ctypes.POINTER(Segment), i32, vp]
@@ -169,6 +171,23 @@ def dequant(pw: PackedWeight) -> torch.Tensor:
     with torch.cuda.device(pw.device):
         _check(lib().q4_0_dequant(pw.data.data_ptr(), pw.n, pw.k, out.data_ptr(), _stream(pw.device)),
                "q4_0_dequant")
+    return out
+
+
+def embed(pw: PackedWeight, ids: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Rows ids of the packed table, dequantized: [len(ids), K] fp32 (NaN rows
+    for ids outside [0, N))."""
+    _dev(ids, "ids", torch.int32)
+    if ids.dim() != 1:
+        raise ValueError("ids must be 1-D")
+    if out is None:
+        out = torch.empty((ids.shape[0], pw.k), dtype=torch.float32, device=ids.device)
+    _dev(out, "out", torch.float32)
+    if tuple(out.shape) != (ids.shape[0], pw.k):
+        raise ValueError("out has the wrong shape")
+    with torch.cuda.device(ids.device):
+        _check(lib().q4_0_embed(pw.data.data_ptr(), pw.n, pw.k, ids.data_ptr(), ids.shape[0], out.data_ptr(),
+                                _stream(ids.device)), "q4_0_embed")
     return out
 
 

@@ -85,6 +85,16 @@ q4_status q4_0_dequant(const void *packed, int64_t N, int64_t K, float *w, void 
     return from_hip(q4::launch_dequant(static_cast<const uint8_t *>(packed), N, K, w, as_stream(stream)));
 }
 
+q4_status q4_0_embed(const void *packed, int64_t N, int64_t K, const int32_t *ids, int64_t n_ids,
+                     float *out, void *stream) {
+    if (!shape_ok(N, K) || n_ids < 0 || n_ids > (int64_t(1) << 24)) return Q4_ERR_SHAPE;
+    if (n_ids == 0) return Q4_OK;
+    if (!packed || !ids || !out) return Q4_ERR_NULL;
+    if (!aligned16(packed) || !aligned16(out) || (reinterpret_cast<uintptr_t>(ids) & 3u)) return Q4_ERR_ALIGN;
+    return from_hip(q4::launch_embed(static_cast<const uint8_t *>(packed), N, K, ids, n_ids, out,
+                                     as_stream(stream)));
+}
+
 q4_status q4_0_linear(const void *x_bf16, int64_t M, const void *packed, int64_t N, int64_t K, float *y,
                       void *stream) {
     q4_0_segment seg;

@@ -184,6 +184,48 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__rest
 
 inline dim3 grid_for(int64_t n) { return dim3(static_cast<unsigned>((n + kThreads - 1) / kThreads)); }
 
+// ---------------------------------------------------------------- embed
+// Row lookup in a packed table: thread t of a looked-up row writes that row's
+// columns 8t .. 8t+7, one 4-byte piece of codes (super-tile kt = t / 16,
+// block i = (t % 16) / 4, lane group g = t % 4) times the block's d.  Row
+// `id` of the table lies at rows id % 16 of its super-tiles.  Consecutive
+// threads write consecutive 32-byte runs of the output row; a grid-stride
+// loop covers any number of ids.  An id outside [0, N) gets a row of NaN
+// and reads nothing.
+__global__ __launch_bounds__(kThreads) void embed_kernel(const uint8_t *__restrict__ nib,
+                                                         const uint16_t *__restrict__ scales,
+                                                         int32_t N, int32_t K, int32_t KT,
+                                                         const int32_t *__restrict__ ids, int64_t total,
+                                                         float *__restrict__ out) {
+    const int per_row = K / 8;
+    for (int64_t t = blockIdx.x * (int64_t)kThreads + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * kThreads) {
+        const int64_t row = t / per_row;
+        const int p = static_cast<int>(t - row * per_row);
+        const int32_t id = ids[row];
+        float v[8];
+        if (id < 0 || id >= N) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = __builtin_nanf("");
+        } else {
+            const int kt = p >> 4, i = (p >> 2) & 3, g = p & 3, r = id & 15;
+            const int64_t T = static_cast<int64_t>(id >> 4) * KT + kt;
+            const uint32_t piece =
+                *reinterpret_cast<const uint32_t *>(nib + T * kTileNibBytes + g * 256 + r * 16 + i * 4);
+            const float d = __half2float(__ushort_as_half(scales[T * kTileScales + r * 4 + i]));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                // sign-extend the 4-bit code: it is q - 8 in two's complement
+                const int c = static_cast<int>(piece << (28 - 4 * j)) >> 28;
+                v[j] = static_cast<float>(c) * d;
+            }
+        }
+        float4 *dst = reinterpret_cast<float4 *>(out + row * K + p * 8);
+        dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+        dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const float *w, int64_t N, int64_t K, uint8_t *out, hipStream_t s) {
@@ -216,6 +258,19 @@ hipError_t launch_dequant(const uint8_t *packed, int64_t N, int64_t K, float *w,
     hipLaunchKernelGGL(dequant_kernel, grid_for(nentries), dim3(kThreads), 0, s, packed,
                        reinterpret_cast<const uint16_t *>(packed + pd.nib_bytes()), (int32_t)N,
                        (int32_t)K, (int32_t)pd.KT, nentries, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_embed(const uint8_t *packed, int64_t N, int64_t K, const int32_t *ids, int64_t n_ids,
+                        float *out, hipStream_t s) {
+    const PackedDims pd(N, K);
+    const int64_t total = n_ids * (K / 8);
+    // enough workgroups to fill the chip several times over; the kernel loops
+    const int64_t want = (total + kThreads - 1) / kThreads;
+    const dim3 grid(static_cast<uint32_t>(want < 65536 ? want : 65536));
+    hipLaunchKernelGGL(embed_kernel, grid, dim3(kThreads), 0, s, packed,
+                       reinterpret_cast<const uint16_t *>(packed + pd.nib_bytes()), (int32_t)N,
+                       (int32_t)K, (int32_t)pd.KT, ids, total, out);
     return hipGetLastError();
 }
 

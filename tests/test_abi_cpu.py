@@ -125,6 +125,21 @@ def test_linear_swiglu_validates_first(L):
     assert b"true" in L.q4_0_linear_swiglu_kernel(1, 3072)        # the gated instantiation
 
 
+def test_embed_validates_first(L):
+    em = L.q4_0_embed
+    assert em(FAKE, 16, 48, FAKE, 4, FAKE, None) == SHAPE          # K % 32
+    assert em(FAKE, 0, 64, FAKE, 4, FAKE, None) == SHAPE           # N < 1
+    assert em(FAKE, 16, 64, FAKE, -1, FAKE, None) == SHAPE         # n_ids < 0
+    assert em(FAKE, 16, 64, FAKE, 2**24 + 1, FAKE, None) == SHAPE
+    assert em(None, 16, 64, FAKE, 4, FAKE, None) == NULL
+    assert em(FAKE, 16, 64, None, 4, FAKE, None) == NULL
+    assert em(FAKE, 16, 64, FAKE, 4, None, None) == NULL
+    assert em(MISALIGNED, 16, 64, FAKE, 4, FAKE, None) == ALIGN
+    assert em(FAKE, 16, 64, FAKE, 4, MISALIGNED, None) == ALIGN
+    assert em(FAKE, 16, 64, FAKE + 2, 4, FAKE, None) == ALIGN        # ids need 4-byte alignment
+    assert em(None, 16, 64, None, 0, None, None) == OK
+
+
 def test_python_binding_raises_on_bad_status(L):
     with pytest.raises(q4.Q4Error) as ei:
         B._check(SHAPE, "q4_0_linear")
