@@ -69,9 +69,10 @@ def test_single_nonzero_nibble(m):
         assert_within_bound(y, O.linear(x, blocks, n, k), O.error_bound(x, blocks, n, k), f"nibble m={m}")
 
 
+@pytest.mark.parametrize("m", [3, 40, 300])
 @pytest.mark.parametrize("e", [-24, -10, 0, 7, 15])
-def test_power_of_two_scales_and_wide_activations(e):
-    n, k, m = 32, 256, 3
+def test_power_of_two_scales_and_wide_activations(e, m):
+    n, k = 32, 256
     rng = np.random.default_rng(e + 50)
     q = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
     sign = np.where(rng.random((n, k // 32)) < 0.5, -1.0, 1.0)
@@ -81,12 +82,12 @@ def test_power_of_two_scales_and_wide_activations(e):
     xf = (rng.standard_normal((m, k)) * np.exp2(rng.integers(-60, 60, size=(m, k)))).astype(np.float32)
     x = inputs.bf16_bits_from_f32(xf)
     pw = device_weight_from_blocks(blocks, n, k)
-    say("pow2 scales", e)
+    say("pow2 scales", e, m)
     y = q4.linear(to_dev_x(x), pw).cpu().numpy()
     assert_within_bound(y, O.linear(x, blocks, n, k), O.error_bound(x, blocks, n, k), f"e={e}")
 
 
-@pytest.mark.parametrize("m", [1, 2, 32, 70])
+@pytest.mark.parametrize("m", [1, 2, 32, 70, 2100])
 def test_reads_no_activation_beyond_k(m):
     """x sits in a larger buffer whose tail is NaN; padded K must not touch it."""
     n, k = 32, 96                                     # K pads to 128 inside the layout
