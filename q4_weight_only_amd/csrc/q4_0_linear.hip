@@ -74,28 +74,6 @@ __device__ __forceinline__ bf16x8 decode_piece(uint32_t w) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Split decode: the fp32 (q - 8) / 16 that v_cvt_off_f32_i4 returns has
-// only 3 significant bits, so its low 16 bits are zero and the register is
-// already a bf16 pair (+0, (q - 8) / 16).  Used as an MFMA operand as is, it
-// carries one weight per pair; the even elements of a piece (low nibbles)
-// and the odd ones (high nibbles) then take one MFMA each, against x with
-// its pairs swapped and as stored.  That drops the pack instructions of
-// decode_piece at the price of a second MFMA per block.
-__device__ __forceinline__ bf16x8 decode_even(uint32_t w) {
-    return __builtin_bit_cast(bf16x8, (floatx4){code_of_byte<0>(w), code_of_byte<1>(w),
-                                                code_of_byte<2>(w), code_of_byte<3>(w)});
-}
-__device__ __forceinline__ bf16x8 decode_odd(uint32_t w) {
-    uint32_t h = w >> 4;
-    asm("" : "+v"(h));
-    return __builtin_bit_cast(bf16x8, (floatx4){code_of_byte<0>(h), code_of_byte<1>(h),
-                                                code_of_byte<2>(h), code_of_byte<3>(h)});
-}
-
-__device__ __forceinline__ floatx4 mfma_acc(const bf16x8 &a, const bf16x8 &b, const floatx4 &c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
     return __half2float(__ushort_as_half(static_cast<unsigned short>(bits16)));
 }
@@ -129,12 +107,10 @@ __device__ __forceinline__ int find_segment(const LinearArgs &a, int tile) {
 // ------------------------------------------------------------------ skinny
 // x staged in LDS: row m of the (padded) x tile starts at m * row_bytes; rows
 // are padded by 16 bytes so the 16 rows read by one MFMA A fragment fall in
-// different LDS banks.  Two copies: x as stored, then x with the two bf16 of
-// every 32-bit pair swapped (the A operand of the even-element MFMA of the
-// split decode).
+// different LDS banks.
 __device__ __forceinline__ int x_row_bytes(int KT) { return KT * kTileK * 2 + 16; }
 
-template <int MROWS, int NT, int WK, int P, bool XLDS, bool SPLIT, int WPE, bool GLU>
+template <int MROWS, int NT, int WK, int P, bool XLDS, int WPE, bool GLU>
 struct SkinnyCfg {
     static constexpr int MT = MROWS > 16 ? 2 : 1;        // 16-row m-tiles
     static constexpr int REGS = MROWS < 4 ? MROWS : 4;   // live accumulator rows per lane
@@ -153,10 +129,10 @@ struct SkinnyCfg {
 // first WK run the gate rows, the last WK the same rows of up, each exactly
 // as a plain launch would; the reduction through LDS sums both in the same
 // wave order and the epilogue stores silu(gate) * up.
-template <int MROWS, int NT, int WK, int P, bool XLDS, bool SPLIT, int WPE, bool GLU>
+template <int MROWS, int NT, int WK, int P, bool XLDS, int WPE, bool GLU>
 __global__ __launch_bounds__(64 * WK * (GLU ? 2 : 1)) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
 void skinny_kernel(const LinearArgs a) {
-    using C = SkinnyCfg<MROWS, NT, WK, P, XLDS, SPLIT, WPE, GLU>;
+    using C = SkinnyCfg<MROWS, NT, WK, P, XLDS, WPE, GLU>;
     constexpr int MT = C::MT, REGS = C::REGS;
     extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
     const int lane = threadIdx.x & 63;
@@ -211,10 +187,10 @@ void skinny_kernel(const LinearArgs a) {
         const int m = mt * 16 + nl;
         a_row[mt] = XLDS ? (m < mrows ? m : mrows - 1) : m;
     }
-    auto load_a = [&](int mt, int b, int copy) -> bf16x8 {
+    auto load_a = [&](int mt, int b) -> bf16x8 {
         if constexpr (XLDS) {
             return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
-                                                  xs + (copy * mrows + a_row[mt]) * row_bytes + (b * kQK + g * 8) * 2));
+                                                  xs + a_row[mt] * row_bytes + (b * kQK + g * 8) * 2));
         } else {
             u32x4 v = (u32x4){0u, 0u, 0u, 0u};
             if (a_row[mt] < a.M && b < nblk)
@@ -234,39 +210,18 @@ void skinny_kernel(const LinearArgs a) {
 #pragma unroll
         for (int i = 0; i < kTileBlocks; ++i) {
             const int b = kt * kTileBlocks + i;
-            if constexpr (XLDS && SPLIT) {
-                bf16x8 Ao[MT], As[MT];
+            bf16x8 A[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) A[mt] = load_a(mt, b);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const bf16x8 B = decode_piece(piece_of(S.nib[nt], i));
+                const float d = scale_of(S.sc[nt], i);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    Ao[mt] = load_a(mt, b, 0);
-                    As[mt] = load_a(mt, b, 1);
-                }
+                    const floatx4 D = mfma_block(A[mt], B);
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const uint32_t w = piece_of(S.nib[nt], i);
-                    const bf16x8 Be = decode_even(w), Bo = decode_odd(w);
-                    const float d = scale_of(S.sc[nt], i);
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const floatx4 D = mfma_acc(Ao[mt], Bo, mfma_block(As[mt], Be));
-#pragma unroll
-                        for (int r = 0; r < REGS; ++r) acc[nt][mt][r] = fmaf(d, D[r], acc[nt][mt][r]);
-                    }
-                }
-            } else {
-                bf16x8 A[MT];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) A[mt] = load_a(mt, b, 0);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const bf16x8 B = decode_piece(piece_of(S.nib[nt], i));
-                    const float d = scale_of(S.sc[nt], i);
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const floatx4 D = mfma_block(A[mt], B);
-#pragma unroll
-                        for (int r = 0; r < REGS; ++r) acc[nt][mt][r] = fmaf(d, D[r], acc[nt][mt][r]);
-                    }
+                    for (int r = 0; r < REGS; ++r) acc[nt][mt][r] = fmaf(d, D[r], acc[nt][mt][r]);
                 }
             }
         }
@@ -277,8 +232,7 @@ void skinny_kernel(const LinearArgs a) {
 #pragma unroll
     for (int p = 0; p < P; ++p)
         if (p < nkt) load_w(st[p], p);
-    // 2. stage x (zero beyond K) while they are in flight: as stored, and
-    //    with each bf16 pair swapped
+    // 2. stage x (zero beyond K) while they are in flight
     if constexpr (XLDS) {
         const int chunks_per_row = KT * (kTileK / 8);          // 16-byte chunks
         const int total = mrows * chunks_per_row;
@@ -287,11 +241,6 @@ void skinny_kernel(const LinearArgs a) {
             u32x4 v = (u32x4){0u, 0u, 0u, 0u};
             if (kc * 8 < a.K) v = *reinterpret_cast<const u32x4 *>(a.x + static_cast<int64_t>(m) * a.K + kc * 8);
             *reinterpret_cast<u32x4 *>(xs + m * row_bytes + kc * 16) = v;
-            if constexpr (SPLIT) {
-                const u32x4 sw = (u32x4){__builtin_amdgcn_alignbit(v.x, v.x, 16), __builtin_amdgcn_alignbit(v.y, v.y, 16),
-                                         __builtin_amdgcn_alignbit(v.z, v.z, 16), __builtin_amdgcn_alignbit(v.w, v.w, 16)};
-                *reinterpret_cast<u32x4 *>(xs + (mrows + m) * row_bytes + kc * 16) = sw;
-            }
         }
         __syncthreads();
     }
@@ -803,15 +752,15 @@ int assign_tiles(LinearArgs &a, int rows_per_tile) {
     return tiles;
 }
 
-template <int MROWS, int NT, int WK, int P, bool SPLIT = true, int WPE = 0, bool GLU = false>
+template <int MROWS, int NT, int WK, int P, int WPE = 0, bool GLU = false>
 hipError_t run_skinny(LinearArgs a, hipStream_t s) {
     const int tiles = assign_tiles<GLU>(a, NT);
     constexpr int kThreads = 64 * WK * (GLU ? 2 : 1);
     constexpr int MT = MROWS > 16 ? 2 : 1;
     const int mrows = a.M < 16 * MT ? a.M : 16 * MT;
-    const uint64_t lds = (SPLIT ? 2 : 1) * static_cast<uint64_t>(mrows) * (static_cast<uint64_t>(a.KT) * kTileK * 2 + 16);
+    const uint64_t lds = static_cast<uint64_t>(mrows) * (static_cast<uint64_t>(a.KT) * kTileK * 2 + 16);
     if (MROWS <= 16 && lds <= kMaxXLds) {
-        auto kernel = skinny_kernel<MROWS, NT, WK, P, true, SPLIT, WPE, GLU>;
+        auto kernel = skinny_kernel<MROWS, NT, WK, P, true, WPE, GLU>;
         static bool raised = false;   // per instantiation: allow the dynamic LDS size once
         if (!raised) {
             const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
@@ -821,7 +770,7 @@ hipError_t run_skinny(LinearArgs a, hipStream_t s) {
         }
         return launch_kernel(kernel, dim3(tiles), dim3(kThreads), static_cast<uint32_t>(lds), s, a);
     }
-    return launch_kernel(skinny_kernel<MROWS, NT, WK, P, false, false, WPE, GLU>, dim3(tiles), dim3(kThreads), 0, s, a);
+    return launch_kernel(skinny_kernel<MROWS, NT, WK, P, false, WPE, GLU>, dim3(tiles), dim3(kThreads), 0, s, a);
 }
 
 template <int MT, int NT, int WM, int WN, int WPE = 0>
@@ -880,12 +829,12 @@ Cfg pick(int64_t M, int64_t K) {
 
 const char *linear_config_name(int64_t M, int64_t K) {
     switch (pick(M, K)) {
-        case Cfg::M1: return "skinny_kernel<1, 1, 4, 2, true, false, 6, false>";
-        case Cfg::M1Long: return "skinny_kernel<1, 1, 8, 3, true, false, 0, false>";
-        case Cfg::M2: return "skinny_kernel<2, 1, 4, 2, true, false, 6, false>";
-        case Cfg::M2Long: return "skinny_kernel<2, 1, 8, 3, true, false, 0, false>";
-        case Cfg::M4: return "skinny_kernel<4, 1, 4, 2, true, false, 0, false>";
-        case Cfg::M16: return "skinny_kernel<16, 1, 4, 2, true, false, 0, false>";
+        case Cfg::M1: return "skinny_kernel<1, 1, 4, 2, true, 6, false>";
+        case Cfg::M1Long: return "skinny_kernel<1, 1, 8, 3, true, 0, false>";
+        case Cfg::M2: return "skinny_kernel<2, 1, 4, 2, true, 6, false>";
+        case Cfg::M2Long: return "skinny_kernel<2, 1, 8, 3, true, 0, false>";
+        case Cfg::M4: return "skinny_kernel<4, 1, 4, 2, true, 0, false>";
+        case Cfg::M16: return "skinny_kernel<16, 1, 4, 2, true, 0, false>";
         case Cfg::M32: return "gemm_kernel<2, 1, 1, 8, 0>";
         case Cfg::M64: return "gemm_kernel<4, 1, 1, 8, 0>";
         case Cfg::Gemm64: return "gemm3_kernel<4, 1, 1, 8, 4, 8, false>";
@@ -895,12 +844,12 @@ const char *linear_config_name(int64_t M, int64_t K) {
 
 hipError_t launch_linear(LinearArgs a, hipStream_t s) {
     switch (pick(a.M, a.K)) {
-        case Cfg::M1: return run_skinny<1, 1, 4, 2, false, 6>(a, s);
-        case Cfg::M1Long: return run_skinny<1, 1, 8, 3, false, 0>(a, s);
-        case Cfg::M2: return run_skinny<2, 1, 4, 2, false, 6>(a, s);
-        case Cfg::M2Long: return run_skinny<2, 1, 8, 3, false, 0>(a, s);
-        case Cfg::M4: return run_skinny<4, 1, 4, 2, false, 0>(a, s);
-        case Cfg::M16: return run_skinny<16, 1, 4, 2, false, 0>(a, s);
+        case Cfg::M1: return run_skinny<1, 1, 4, 2, 6>(a, s);
+        case Cfg::M1Long: return run_skinny<1, 1, 8, 3, 0>(a, s);
+        case Cfg::M2: return run_skinny<2, 1, 4, 2, 6>(a, s);
+        case Cfg::M2Long: return run_skinny<2, 1, 8, 3, 0>(a, s);
+        case Cfg::M4: return run_skinny<4, 1, 4, 2, 0>(a, s);
+        case Cfg::M16: return run_skinny<16, 1, 4, 2, 0>(a, s);
         case Cfg::M32: return run_gemm<2, 1, 1, 8, 0>(a, s);
         case Cfg::M64: return run_gemm<4, 1, 1, 8, 0>(a, s);
         case Cfg::Gemm64: return run_gemm3<4, 1, 1, 8, 4, 8>(a, s);
@@ -913,12 +862,12 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
 // waves and WN / 2 up waves), so every wave runs the plain arithmetic.
 const char *linear_glu_config_name(int64_t M, int64_t K) {
     switch (pick(M, K)) {
-        case Cfg::M1: return "skinny_kernel<1, 1, 4, 2, true, false, 6, true>";
-        case Cfg::M1Long: return "skinny_kernel<1, 1, 8, 3, true, false, 0, true>";
-        case Cfg::M2: return "skinny_kernel<2, 1, 4, 2, true, false, 6, true>";
-        case Cfg::M2Long: return "skinny_kernel<2, 1, 8, 3, true, false, 0, true>";
-        case Cfg::M4: return "skinny_kernel<4, 1, 4, 2, true, false, 0, true>";
-        case Cfg::M16: return "skinny_kernel<16, 1, 4, 2, true, false, 0, true>";
+        case Cfg::M1: return "skinny_kernel<1, 1, 4, 2, true, 6, true>";
+        case Cfg::M1Long: return "skinny_kernel<1, 1, 8, 3, true, 0, true>";
+        case Cfg::M2: return "skinny_kernel<2, 1, 4, 2, true, 6, true>";
+        case Cfg::M2Long: return "skinny_kernel<2, 1, 8, 3, true, 0, true>";
+        case Cfg::M4: return "skinny_kernel<4, 1, 4, 2, true, 0, true>";
+        case Cfg::M16: return "skinny_kernel<16, 1, 4, 2, true, 0, true>";
         case Cfg::M32: return "gemm3_kernel<2, 1, 1, 8, 0, 8, true>";
         case Cfg::M64: return "gemm3_kernel<4, 1, 1, 8, 0, 8, true>";
         case Cfg::Gemm64: return "gemm3_kernel<4, 1, 1, 8, 4, 8, true>";
@@ -928,12 +877,12 @@ const char *linear_glu_config_name(int64_t M, int64_t K) {
 
 hipError_t launch_linear_glu(LinearArgs a, hipStream_t s) {
     switch (pick(a.M, a.K)) {
-        case Cfg::M1: return run_skinny<1, 1, 4, 2, false, 6, true>(a, s);
-        case Cfg::M1Long: return run_skinny<1, 1, 8, 3, false, 0, true>(a, s);
-        case Cfg::M2: return run_skinny<2, 1, 4, 2, false, 6, true>(a, s);
-        case Cfg::M2Long: return run_skinny<2, 1, 8, 3, false, 0, true>(a, s);
-        case Cfg::M4: return run_skinny<4, 1, 4, 2, false, 0, true>(a, s);
-        case Cfg::M16: return run_skinny<16, 1, 4, 2, false, 0, true>(a, s);
+        case Cfg::M1: return run_skinny<1, 1, 4, 2, 6, true>(a, s);
+        case Cfg::M1Long: return run_skinny<1, 1, 8, 3, 0, true>(a, s);
+        case Cfg::M2: return run_skinny<2, 1, 4, 2, 6, true>(a, s);
+        case Cfg::M2Long: return run_skinny<2, 1, 8, 3, 0, true>(a, s);
+        case Cfg::M4: return run_skinny<4, 1, 4, 2, 0, true>(a, s);
+        case Cfg::M16: return run_skinny<16, 1, 4, 2, 0, true>(a, s);
         case Cfg::M32: return run_gemm3<2, 1, 1, 8, 0, 8, true>(a, s);
         case Cfg::M64: return run_gemm3<4, 1, 1, 8, 0, 8, true>(a, s);
         case Cfg::Gemm64: return run_gemm3<4, 1, 1, 8, 4, 8, true>(a, s);
