@@ -227,11 +227,12 @@ def time_swiglu(prepared, ms, reps, dev):
         xb = spec0.activations(m)
         x = torch.from_numpy(xb.view(np.int16).copy()).to(dev).view(torch.bfloat16)
         h = torch.empty((m, n), dtype=torch.float32, device=dev)
+        h16 = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for _ in range(2)]
-        pairs = {"fused": [], "unfused": []}
+        pairs = {"fused": [], "fused_bf16": [], "unfused": []}
         for r in range(reps + 1):
             for _, pws in gate_up:
-                for kind in ("fused", "unfused"):
+                for kind in ("fused", "fused_bf16", "unfused"):
                     a = torch.cuda.Event(enable_timing=True)
                     b = torch.cuda.Event(enable_timing=True)
                     a.record(stream)
@@ -239,6 +240,8 @@ def time_swiglu(prepared, ms, reps, dev):
                     q4.time_next_launch(a, b)
                     if kind == "fused":
                         q4.linear_swiglu(x, pws[0], pws[1], h)
+                    elif kind == "fused_bf16":
+                        q4.linear_swiglu(x, pws[0], pws[1], h16, dtype=torch.bfloat16)
                     else:
                         q4.linear_multi(x, pws, ys)
                     if r > 0:              # the first round warms up
@@ -252,6 +255,7 @@ def time_swiglu(prepared, ms, reps, dev):
         out[f"M={m}"] = {
             "kernel": q4.linear_swiglu_kernel(m, k),
             "fused_us": round(t["fused"] * 1e6, 2),
+            "fused_bf16_out_us": round(t["fused_bf16"] * 1e6, 2),
             "unfused_us": round(t["unfused"] * 1e6, 2),
             "fused_GBs": round(fused_bytes / t["fused"] / 1e9, 1),
             "unfused_GBs": round(unfused_bytes / t["unfused"] / 1e9, 1),
@@ -495,7 +499,7 @@ def main():
     if not args.no_swiglu:
         out["swiglu"] = {
             "workload": "decoder gate/up 3072->2x9216 (one weight pair per layer, rotated), "
-                        "h = silu(x Wg^T) * (x Wu^T) fp32",
+                        "h = silu(x Wg^T) * (x Wu^T), fp32 out (fused_bf16_out_us: bf16 out)",
             **time_swiglu(prepared, (1, 2, 2048), 3 if args.layers >= 8 else 6, dev),
         }
         log(f"swiglu: {out['swiglu']}")

@@ -155,16 +155,19 @@ q4_status q4_0_linear_multi(const void *x_bf16, int64_t M, int64_t K, const q4_0
  *   silu(t) = t / (1 + e^-t),
  *
  * with gate_packed (Wg) and up_packed (Wu) packed [N, K] matrices of the same
- * shape and h fp32 [M, N] (device, row-major).  One launch; g and u never
- * reach memory, so the output is half the bytes of a gate/up
- * q4_0_linear_multi.  g and u are computed exactly as q4_0_linear computes
- * them, and silu and the product in fp32, so h is within
+ * shape and h [M, N] (device, row-major): fp32 when h_bf16 == 0, bf16 (the
+ * fp32 value rounded to nearest even, ready to be the x of the down
+ * projection) when h_bf16 == 1; other values are Q4_ERR_SHAPE.  One launch;
+ * g and u never reach memory, so the output is at most half the bytes of a
+ * gate/up q4_0_linear_multi.  g and u are computed exactly as q4_0_linear
+ * computes them, and silu and the product in fp32, so the fp32 h is within
  * 1.1 bg (|u| + bu) + |silu(g)| bu + 1e-5 |h| of the exact value, where bg
- * and bu are the q4_0_linear bounds of g and u.  Arguments are validated as
- * for q4_0_linear (both weight pointers); deterministic.
+ * and bu are the q4_0_linear bounds of g and u (bf16: plus 2^-9 |h|).
+ * Arguments are validated as for q4_0_linear (both weight pointers);
+ * deterministic.
  */
 q4_status q4_0_linear_swiglu(const void *x_bf16, int64_t M, int64_t K, const void *gate_packed,
-                             const void *up_packed, int64_t N, float *h, void *stream);
+                             const void *up_packed, int64_t N, void *h, int h_bf16, void *stream);
 
 /* Name of the kernel instantiation q4_0_linear_swiglu runs for M and K
  * (static string; "" for an invalid M or K). */

@@ -70,7 +70,7 @@ def lib() -> ctypes.CDLL:
             L.q4_0_linear_multi.restype = i32
             L.q4_0_linear_kernel.argtypes = [i64, i64]
             L.q4_0_linear_kernel.restype = ctypes.c_char_p
-            L.q4_0_linear_swiglu.argtypes = [vp, i64, i64, vp, vp, i64, vp, vp]
+            L.q4_0_linear_swiglu.argtypes = [vp, i64, i64, vp, vp, i64, vp, i32, vp]
             L.q4_0_linear_swiglu.restype = i32
             L.q4_0_linear_swiglu_kernel.argtypes = [i64, i64]
             L.q4_0_linear_swiglu_kernel.restype = ctypes.c_char_p
@@ -233,22 +233,26 @@ def linear_multi(x: torch.Tensor, weights, outs=None):
 
 
 def linear_swiglu(x: torch.Tensor, gate: PackedWeight, up: PackedWeight,
-                  out: torch.Tensor | None = None) -> torch.Tensor:
-    """h [M, N] fp32 = silu(x Wg^T) * (x Wu^T) in one launch (gate and up [N, K])."""
+                  out: torch.Tensor | None = None, dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """h [M, N] = silu(x Wg^T) * (x Wu^T) in one launch (gate and up [N, K]);
+    h is fp32, or bf16 (rounded to nearest even) with dtype=torch.bfloat16."""
     _dev(x, "x", torch.bfloat16)
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("dtype must be torch.float32 or torch.bfloat16")
     if gate.n != up.n or gate.k != up.k:
         raise ValueError("gate and up must have the same shape")
     if x.dim() != 2 or x.shape[1] != gate.k:
         raise ValueError(f"x must be [M, {gate.k}]")
     m = x.shape[0]
     if out is None:
-        out = torch.empty((m, gate.n), dtype=torch.float32, device=x.device)
-    _dev(out, "out", torch.float32)
+        out = torch.empty((m, gate.n), dtype=dtype, device=x.device)
+    _dev(out, "out", dtype)
     if tuple(out.shape) != (m, gate.n):
         raise ValueError("out has the wrong shape")
     with torch.cuda.device(x.device):
         _check(lib().q4_0_linear_swiglu(x.data_ptr(), m, gate.k, gate.data.data_ptr(), up.data.data_ptr(),
-                                        gate.n, out.data_ptr(), _stream(x.device)), "q4_0_linear_swiglu")
+                                        gate.n, out.data_ptr(), int(dtype == torch.bfloat16), _stream(x.device)),
+               "q4_0_linear_swiglu")
     return out
 
 

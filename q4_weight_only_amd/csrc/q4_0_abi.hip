@@ -124,13 +124,15 @@ q4_status q4_0_linear_multi(const void *x_bf16, int64_t M, int64_t K, const q4_0
     a.K = static_cast<int32_t>(K);
     a.KT = static_cast<int32_t>(q4::round_up(K, q4::kTileK) / q4::kTileK);
     a.nseg = nseg;
+    a.y_bf16 = 0;
     for (int i = 0; i < q4::kMaxSegments; ++i) a.seg[i] = q4::Segment{};
     for (int i = 0; i < nseg; ++i) a.seg[i] = make_segment(segs[i].packed, segs[i].N, K, segs[i].y);
     return from_hip(q4::launch_linear(a, as_stream(stream)));
 }
 
 q4_status q4_0_linear_swiglu(const void *x_bf16, int64_t M, int64_t K, const void *gate_packed,
-                             const void *up_packed, int64_t N, float *h, void *stream) {
+                             const void *up_packed, int64_t N, void *h, int h_bf16, void *stream) {
+    if (h_bf16 != 0 && h_bf16 != 1) return Q4_ERR_SHAPE;
     if (M < 0 || M > kMaxM || !shape_ok(N, K)) return Q4_ERR_SHAPE;
     if (M == 0) return Q4_OK;
     if (!x_bf16 || !gate_packed || !up_packed || !h) return Q4_ERR_NULL;
@@ -142,8 +144,9 @@ q4_status q4_0_linear_swiglu(const void *x_bf16, int64_t M, int64_t K, const voi
     a.K = static_cast<int32_t>(K);
     a.KT = static_cast<int32_t>(q4::round_up(K, q4::kTileK) / q4::kTileK);
     a.nseg = 2;
+    a.y_bf16 = h_bf16;
     for (int i = 0; i < q4::kMaxSegments; ++i) a.seg[i] = q4::Segment{};
-    a.seg[0] = make_segment(gate_packed, N, K, h);
+    a.seg[0] = make_segment(gate_packed, N, K, static_cast<float *>(h));
     a.seg[1] = make_segment(up_packed, N, K, nullptr);
     return from_hip(q4::launch_linear_glu(a, as_stream(stream)));
 }

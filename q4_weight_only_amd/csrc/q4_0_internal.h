@@ -44,6 +44,7 @@ struct LinearArgs {
     int32_t K;               // true K (multiple of 32)
     int32_t KT;              // padded K / 128
     int32_t nseg;
+    int32_t y_bf16;          // gated launches: store h as bf16 (RNE) instead of fp32
     Segment seg[kMaxSegments];
 };
 

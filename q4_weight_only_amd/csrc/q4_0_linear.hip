@@ -32,6 +32,7 @@
 // No kernel uses atomics: results are bitwise reproducible.
 
 #include <hip/hip_ext.h>
+#include <hip/hip_bf16.h>
 #include <hip/hip_fp16.h>
 
 #include "q4_0_internal.h"
@@ -94,6 +95,15 @@ __device__ __forceinline__ floatx4 mfma_block(const bf16x8 &a, const bf16x8 &b) 
 // silu(g) = g / (1 + e^-g) in fp32 (expf overflows to +inf for g below
 // about -88, which gives -0: the true value is below 1e-36 there).
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+// Epilogue store of one output: fp32, or for a gated launch that asks for it
+// bf16 rounded to nearest even (the y pointer then addresses bf16 elements).
+__device__ __forceinline__ void store_out(const LinearArgs &a, const Segment &sg, int64_t idx, float v) {
+    if (a.y_bf16)
+        reinterpret_cast<__hip_bfloat16 *>(sg.y)[idx] = __float2bfloat16(v);
+    else
+        sg.y[idx] = v;
+}
 
 // Segment lookup: the segments' work tiles are laid end to end.
 __device__ __forceinline__ int find_segment(const LinearArgs &a, int tile) {
@@ -315,7 +325,10 @@ void skinny_kernel(const LinearArgs a) {
                 const int m = mt * 16 + 4 * g + r;
                 if (m >= a.M) continue;
                 const float v = acc[nt][mt][r] * 16.0f;
-                sg.y[static_cast<int64_t>(m) * sg.N + n] = GLU ? silu_f32(v) * (up[nt][mt][r] * 16.0f) : v;
+                if constexpr (GLU)
+                    store_out(a, sg, static_cast<int64_t>(m) * sg.N + n, silu_f32(v) * (up[nt][mt][r] * 16.0f));
+                else
+                    sg.y[static_cast<int64_t>(m) * sg.N + n] = v;
             }
     }
 }
@@ -705,8 +718,11 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
                 const int m = m0 + (wm * MT + mt) * 16 + 4 * g + r;
                 if (m >= a.M) continue;
                 const float v = acc[mt][nt][r] * 16.0f;
-                sg.y[static_cast<int64_t>(m) * sg.N + n] =
-                    GLU ? silu_f32(v) * (xch[((mt * NT + nt) * 4 + r) * 64 + lane] * 16.0f) : v;
+                if constexpr (GLU)
+                    store_out(a, sg, static_cast<int64_t>(m) * sg.N + n,
+                              silu_f32(v) * (xch[((mt * NT + nt) * 4 + r) * 64 + lane] * 16.0f));
+                else
+                    sg.y[static_cast<int64_t>(m) * sg.N + n] = v;
             }
     }
 }

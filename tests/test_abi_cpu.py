@@ -109,18 +109,19 @@ def test_linear_multi_validates_first(L):
 
 def test_linear_swiglu_validates_first(L):
     sw = L.q4_0_linear_swiglu
-    assert sw(FAKE, 1, 48, FAKE, FAKE, 16, FAKE, None) == SHAPE       # K % 32
-    assert sw(FAKE, -1, 64, FAKE, FAKE, 16, FAKE, None) == SHAPE      # M < 0
-    assert sw(FAKE, 1, 64, FAKE, FAKE, 0, FAKE, None) == SHAPE        # N < 1
-    assert sw(FAKE, 1, 64, FAKE, FAKE, 2**30 + 1, FAKE, None) == SHAPE
-    assert sw(None, 1, 64, FAKE, FAKE, 16, FAKE, None) == NULL
-    assert sw(FAKE, 1, 64, None, FAKE, 16, FAKE, None) == NULL
-    assert sw(FAKE, 1, 64, FAKE, None, 16, FAKE, None) == NULL
-    assert sw(FAKE, 1, 64, FAKE, FAKE, 16, None, None) == NULL
-    assert sw(MISALIGNED, 1, 64, FAKE, FAKE, 16, FAKE, None) == ALIGN
-    assert sw(FAKE, 1, 64, FAKE, MISALIGNED, 16, FAKE, None) == ALIGN
-    assert sw(FAKE, 1, 64, FAKE, FAKE, 16, MISALIGNED, None) == ALIGN
-    assert sw(None, 0, 64, None, None, 16, None, None) == OK
+    assert sw(FAKE, 1, 48, FAKE, FAKE, 16, FAKE, 0, None) == SHAPE       # K % 32
+    assert sw(FAKE, -1, 64, FAKE, FAKE, 16, FAKE, 0, None) == SHAPE      # M < 0
+    assert sw(FAKE, 1, 64, FAKE, FAKE, 0, FAKE, 0, None) == SHAPE        # N < 1
+    assert sw(FAKE, 1, 64, FAKE, FAKE, 2**30 + 1, FAKE, 0, None) == SHAPE
+    assert sw(FAKE, 1, 64, FAKE, FAKE, 16, FAKE, 2, None) == SHAPE       # output type flag
+    assert sw(None, 1, 64, FAKE, FAKE, 16, FAKE, 1, None) == NULL
+    assert sw(FAKE, 1, 64, None, FAKE, 16, FAKE, 0, None) == NULL
+    assert sw(FAKE, 1, 64, FAKE, None, 16, FAKE, 0, None) == NULL
+    assert sw(FAKE, 1, 64, FAKE, FAKE, 16, None, 0, None) == NULL
+    assert sw(MISALIGNED, 1, 64, FAKE, FAKE, 16, FAKE, 0, None) == ALIGN
+    assert sw(FAKE, 1, 64, FAKE, MISALIGNED, 16, FAKE, 0, None) == ALIGN
+    assert sw(FAKE, 1, 64, FAKE, FAKE, 16, MISALIGNED, 1, None) == ALIGN
+    assert sw(None, 0, 64, None, None, 16, None, 0, None) == OK
     assert L.q4_0_linear_swiglu_kernel(0, 64) == b""
     assert b"true" in L.q4_0_linear_swiglu_kernel(1, 3072)        # the gated instantiation
 

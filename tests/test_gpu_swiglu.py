@@ -112,3 +112,24 @@ def test_swiglu_deterministic_and_empty():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     empty = q4.linear_swiglu(x[:0], gpw, upw)
     assert tuple(empty.shape) == (0, n)
+
+
+@pytest.mark.parametrize("m", [1, 2, 16, 40, 2048])
+def test_swiglu_bf16_output(m):
+    """bf16 output is the fp32 output rounded to nearest even, bit for bit, and
+    so within bound + 2^-9 (|h| + bound) of the exact value."""
+    n, k = 264, 1024
+    gw, uw = _pair(n, k, 36)
+    xb = inputs.activations_bf16((m, k), seed=36, tags=(m,))
+    x = to_dev_x(xb)
+    gpw, gblk = device_weight_from_f32(gw)
+    upw, ublk = device_weight_from_f32(uw)
+    say("swiglu bf16", m)
+    h32 = q4.linear_swiglu(x, gpw, upw)
+    h16 = q4.linear_swiglu(x, gpw, upw, dtype=torch.bfloat16)
+    assert h16.dtype == torch.bfloat16
+    assert torch.equal(h16.view(torch.int16), h32.to(torch.bfloat16).view(torch.int16))
+    gb, ub = gblk.cpu().numpy(), ublk.cpu().numpy()
+    ref = O.swiglu(xb, gb, ub, n, k)
+    bound = O.swiglu_bound(xb, gb, ub, n, k)
+    assert_within_bound(h16.float().cpu().numpy(), ref, bound + 2.0**-9 * (np.abs(ref) + bound), f"bf16 M={m}")
