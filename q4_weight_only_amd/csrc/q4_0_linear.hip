@@ -642,12 +642,18 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
         for (int nt = 0; nt < NT; ++nt) {
             const bf16x8 B = decode_piece(piece_of(S.nib[nt], i));
             const float d = scale_of(S.sc[nt], i);
+            // each MFMA's rescale is issued after the next MFMA, so the FMAs
+            // never wait on a result still in the matrix pipe
+            floatx4 D[MT];
+            D[0] = mfma_block(A[0], B);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const floatx4 D = mfma_block(A[mt], B);
+            for (int mt = 1; mt < MT; ++mt) {
+                D[mt] = mfma_block(A[mt], B);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[mt][nt][r] = fmaf(d, D[r], acc[mt][nt][r]);
+                for (int r = 0; r < 4; ++r) acc[mt - 1][nt][r] = fmaf(d, D[mt - 1][r], acc[mt - 1][nt][r]);
             }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[MT - 1][nt][r] = fmaf(d, D[MT - 1][r], acc[MT - 1][nt][r]);
         }
         // one block at a time: bounds the live MFMA results and operands
         __builtin_amdgcn_sched_barrier(0);
