@@ -23,6 +23,8 @@ Printed (one JSON line):
               (kernel-own times over the 26 layers' gate/up weights)
   embed       Q4 embedding lookups (q4_0_embed) of 32, 2048 and 16384 random ids
               from the 131072 x 3072 table: time per launch and GB/s moved
+  lm_head     the same table as the LM head linear at M = 1 and 32 (kernel-own
+              times, each launch after a 512 MiB read so the table comes from HBM)
   cpu_baseline  the CPU oracle (dequantize + fp64 matmul) on a bounded sample
               of the same step, on the host cores
 """
@@ -304,6 +306,45 @@ def time_embed(pw, counts, reps, dev):
     return out
 
 
+def time_lm_head(spec, pw, ms, reps, dev):
+    """The 131072 x 3072 LM head as a single linear at each M: kernel-own time
+    (armed events) of launches that each follow a read of a 512 MiB buffer,
+    so the table streams from HBM rather than from the 256 MB infinity cache
+    (a read, not a fill, so no write-back competes with the launch)."""
+    import numpy as np
+    import torch
+
+    import q4_weight_only_amd as q4
+
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for m in ms:
+        xb = spec.activations(m)
+        x = torch.from_numpy(xb.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+        y = torch.empty((m, pw.n), dtype=torch.float32, device=dev)
+        q4.linear(x, pw, y)
+        pairs = []
+        for _ in range(reps):
+            torch.sum(flush, dim=0, out=sink)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            b.record(stream)
+            q4.time_next_launch(a, b)
+            q4.linear(x, pw, y)
+            pairs.append((a, b))
+        torch.cuda.synchronize(dev)
+        t = float(np.median([a.elapsed_time(b) / 1e3 for a, b in pairs]))
+        moved = algorithmic_bytes(spec, m)
+        out[f"M={m}"] = {"kernel": q4.linear_kernel(m, spec.K), "us": round(t * 1e6, 2),
+                         "GBs": round(moved / t / 1e9, 1), "frac_of_8TBs": round(moved / t / 1e9 / HBM_PEAK_GBS, 4),
+                         "TFLOPs": round(flops(spec, m) / t / 1e12, 2), "launches": reps}
+    del flush, sink
+    return out
+
+
 def kernel_source_digest():
     h = hashlib.sha256()
     for f in ("q4_0_linear.hip", "q4_0_internal.h"):
@@ -514,6 +555,12 @@ def main():
             **time_embed(lm_pws[0], (32, 2048, 16384), 50, dev),
         }
         log(f"embed: {out['embed']}")
+        # the same table as the LM head linear (workload 3: M = 1 and 32)
+        out["lm_head"] = {
+            "workload": f"LM head {lm_spec.K}->{lm_spec.Ns[0]} (226 MB of Q4_0), one launch, streamed from HBM",
+            **time_lm_head(lm_spec, lm_pws[0], (1, 32), 10, dev),
+        }
+        log(f"lm_head: {out['lm_head']}")
         del lm_pws
 
     if args.copy_calibration:
