@@ -27,8 +27,10 @@
  *     the caller synchronizes it.
  *   - Every argument is checked before any HIP call.  On a bad argument the
  *     call returns a nonzero q4_status and launches nothing.  A failed launch
- *     returns Q4_ERR_HIP.  A device fault surfaces at the caller's next
- *     synchronization.  Nothing aborts.
+ *     returns Q4_ERR_HIP, and so does a shape inside the limits below whose
+ *     launch would need more than 2^31 - 1 workgroups (only matrices far
+ *     larger than any device memory).  A device fault surfaces at the
+ *     caller's next synchronization.  Nothing aborts.
  *   - Device pointers to x, y, packed, GGUF blocks and fp32 weights must be
  *     16-byte aligned (any torch allocation is).  GGUF block buffers are
  *     N * K/32 * 18 bytes, contiguous.

@@ -182,7 +182,15 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__rest
     }
 }
 
-inline dim3 grid_for(int64_t n) { return dim3(static_cast<unsigned>((n + kThreads - 1) / kThreads)); }
+// One thread per item; a count needing more than 2^31 - 1 workgroups (far
+// beyond any matrix that fits in memory) is refused rather than truncated.
+constexpr int64_t kMaxGrid = 0x7fffffff;
+inline bool grid_for(int64_t n, dim3 &grid) {
+    const int64_t blocks = (n + kThreads - 1) / kThreads;
+    if (blocks > kMaxGrid) return false;
+    grid = dim3(static_cast<unsigned>(blocks));
+    return true;
+}
 
 // ---------------------------------------------------------------- embed
 // Row lookup in a packed table: thread t of a looked-up row writes that row's
@@ -230,14 +238,18 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(const uint8_t *__restri
 
 hipError_t launch_quantize(const float *w, int64_t N, int64_t K, uint8_t *out, hipStream_t s) {
     const int64_t nblocks = N * (K / kQK);
-    hipLaunchKernelGGL(quantize_kernel, grid_for(nblocks), dim3(kThreads), 0, s, w, nblocks, out);
+    dim3 grid;
+    if (!grid_for(nblocks, grid)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quantize_kernel, grid, dim3(kThreads), 0, s, w, nblocks, out);
     return hipGetLastError();
 }
 
 hipError_t launch_pack(const uint8_t *gguf, int64_t N, int64_t K, uint8_t *packed, hipStream_t s) {
     const PackedDims pd(N, K);
     const int64_t nentries = pd.RT * pd.KT * 64;
-    hipLaunchKernelGGL(pack_kernel, grid_for(nentries), dim3(kThreads), 0, s, gguf, (int32_t)N,
+    dim3 grid;
+    if (!grid_for(nentries, grid)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pack_kernel, grid, dim3(kThreads), 0, s, gguf, (int32_t)N,
                        (int32_t)K, (int32_t)pd.KT, nentries, packed,
                        reinterpret_cast<uint16_t *>(packed + pd.nib_bytes()));
     return hipGetLastError();
@@ -246,7 +258,9 @@ hipError_t launch_pack(const uint8_t *gguf, int64_t N, int64_t K, uint8_t *packe
 hipError_t launch_unpack(const uint8_t *packed, int64_t N, int64_t K, uint8_t *gguf, hipStream_t s) {
     const PackedDims pd(N, K);
     const int64_t nentries = pd.RT * pd.KT * 64;
-    hipLaunchKernelGGL(unpack_kernel, grid_for(nentries), dim3(kThreads), 0, s, packed,
+    dim3 grid;
+    if (!grid_for(nentries, grid)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(unpack_kernel, grid, dim3(kThreads), 0, s, packed,
                        reinterpret_cast<const uint16_t *>(packed + pd.nib_bytes()), (int32_t)N,
                        (int32_t)K, (int32_t)pd.KT, nentries, gguf);
     return hipGetLastError();
@@ -255,7 +269,9 @@ hipError_t launch_unpack(const uint8_t *packed, int64_t N, int64_t K, uint8_t *g
 hipError_t launch_dequant(const uint8_t *packed, int64_t N, int64_t K, float *w, hipStream_t s) {
     const PackedDims pd(N, K);
     const int64_t nentries = pd.RT * pd.KT * 64;
-    hipLaunchKernelGGL(dequant_kernel, grid_for(nentries), dim3(kThreads), 0, s, packed,
+    dim3 grid;
+    if (!grid_for(nentries, grid)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(dequant_kernel, grid, dim3(kThreads), 0, s, packed,
                        reinterpret_cast<const uint16_t *>(packed + pd.nib_bytes()), (int32_t)N,
                        (int32_t)K, (int32_t)pd.KT, nentries, w);
     return hipGetLastError();

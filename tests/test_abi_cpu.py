@@ -141,6 +141,17 @@ def test_embed_validates_first(L):
     assert em(None, 16, 64, None, 0, None, None) == OK
 
 
+def test_format_grids_beyond_the_limit_are_refused(L):
+    """A matrix within the shape limits but needing more than 2^31 - 1
+    workgroups is refused before any HIP call (Q4_ERR_HIP), not truncated."""
+    HIP = 5
+    n, k = 2**30, 2**20
+    assert L.q4_0_quantize(FAKE, n, k, FAKE, None) == HIP
+    assert L.q4_0_pack(FAKE, n, k, FAKE, None) == HIP
+    assert L.q4_0_unpack(FAKE, n, k, FAKE, None) == HIP
+    assert L.q4_0_dequant(FAKE, n, k, FAKE, None) == HIP
+
+
 def test_python_binding_raises_on_bad_status(L):
     with pytest.raises(q4.Q4Error) as ei:
         B._check(SHAPE, "q4_0_linear")
