@@ -558,7 +558,7 @@ def main():
         # the same table as the LM head linear (workload 3: M = 1 and 32)
         out["lm_head"] = {
             "workload": f"LM head {lm_spec.K}->{lm_spec.Ns[0]} (226 MB of Q4_0), one launch, streamed from HBM",
-            **time_lm_head(lm_spec, lm_pws[0], (1, 32), 10, dev),
+            **time_lm_head(lm_spec, lm_pws[0], (1, 32), 20, dev),
         }
         log(f"lm_head: {out['lm_head']}")
         del lm_pws

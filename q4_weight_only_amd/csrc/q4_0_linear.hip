@@ -31,6 +31,8 @@
 // order, so they give bitwise equal results for any tiling.
 // No kernel uses atomics: results are bitwise reproducible.
 
+#include <atomic>
+
 #include <hip/hip_ext.h>
 #include <hip/hip_bf16.h>
 #include <hip/hip_fp16.h>
@@ -752,9 +754,33 @@ hipError_t launch_kernel(Kernel kernel, dim3 grid, dim3 block, uint32_t lds, hip
     return hipGetLastError();
 }
 
-// Tile configurations depend on M only, so a fused multi-segment launch and
-// separate single launches run the same arithmetic in the same order.
-constexpr uint32_t kMaxXLds = 128 * 1024;  // dynamic LDS budget for staged x (both copies)
+// Tile configurations depend on M and K only, so a fused multi-segment launch
+// and separate single launches run the same arithmetic in the same order.
+
+// x is staged in LDS when it fits a budget that keeps several workgroups on
+// a CU: up to 4 rows it may take 128 KiB (x is small next to the weights);
+// for more rows 48 KiB, since a 16-row x of 3072 columns (98 KiB) would leave
+// room for one workgroup per CU, and those rows then read x from L2 instead.
+constexpr uint32_t kMaxXLds = 128 * 1024;
+constexpr uint64_t xlds_budget(int mrows_max) { return mrows_max <= 4 ? kMaxXLds : 48 * 1024; }
+inline uint64_t skinny_x_bytes(int64_t M, int64_t K, int mrows_max) {
+    const int64_t mrows = M < mrows_max ? M : mrows_max;
+    return static_cast<uint64_t>(mrows) * static_cast<uint64_t>((K + kTileK - 1) / kTileK * kTileK * 2 + 16);
+}
+
+// hipFuncSetAttribute (the dynamic LDS limit) is applied once per device
+// and kernel instantiation.
+template <typename Kernel>
+hipError_t allow_dynamic_lds(Kernel kernel, std::atomic<uint64_t> &done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = uint64_t(1) << (dev & 63);
+    if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, kMaxXLds);
+    if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
 
 // Work tiles of a launch: the segments' tiles laid end to end, each tile
 // covering `rows_per_tile` 16-row tiles; a gated launch tiles the gate rows
@@ -778,18 +804,13 @@ template <int MROWS, int NT, int WK, int P, int WPE = 0, bool GLU = false>
 hipError_t run_skinny(LinearArgs a, hipStream_t s) {
     const int tiles = assign_tiles<GLU>(a, NT);
     constexpr int kThreads = 64 * WK * (GLU ? 2 : 1);
-    constexpr int MT = MROWS > 16 ? 2 : 1;
-    const int mrows = a.M < 16 * MT ? a.M : 16 * MT;
-    const uint64_t lds = static_cast<uint64_t>(mrows) * (static_cast<uint64_t>(a.KT) * kTileK * 2 + 16);
-    if (MROWS <= 16 && lds <= kMaxXLds) {
+    static_assert(MROWS <= 16, "x staging covers one 16-row m-tile");
+    const uint64_t lds = skinny_x_bytes(a.M, a.K, MROWS);
+    if (lds <= xlds_budget(MROWS)) {
         auto kernel = skinny_kernel<MROWS, NT, WK, P, true, WPE, GLU>;
-        static bool raised = false;   // per instantiation: allow the dynamic LDS size once
-        if (!raised) {
-            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kMaxXLds);
-            if (e != hipSuccess) return e;
-            raised = true;
-        }
+        static std::atomic<uint64_t> lds_allowed{0};
+        const hipError_t e = allow_dynamic_lds(kernel, lds_allowed);
+        if (e != hipSuccess) return e;
         return launch_kernel(kernel, dim3(tiles), dim3(kThreads), static_cast<uint32_t>(lds), s, a);
     }
     return launch_kernel(skinny_kernel<MROWS, NT, WK, P, false, WPE, GLU>, dim3(tiles), dim3(kThreads), 0, s, a);
@@ -829,34 +850,41 @@ void arm_launch_events(hipEvent_t start, hipEvent_t stop) {
     t_stop_event = stop;
 }
 
-// The dispatch table: kernel configuration by M (and K for M <= 2).  Decode
-// sizes use short K-slices per wave and a shallow prefetch so that many waves
-// stay resident (the launches are latency-bound); long rows split K wider.
-// Above 64 rows the GEMM takes 64-row tiles below 2048 rows (more workgroups
-// for the 1.5k-row audio shapes) and 128-row tiles from there on.
+// The dispatch table: kernel configuration by M and K.  Decode sizes split K
+// over the waves of a workgroup with a short prefetch, so that many waves
+// stay resident (the launches are latency-bound); long rows (K > 3072) split
+// K wider.  Above 64 rows the GEMM takes 64-row tiles below 2048 rows (more
+// workgroups for the 1.5k-row audio shapes) and 128-row tiles from there on.
 namespace {
-enum class Cfg { M1, M1Long, M2, M2Long, M4, M16, M32, M64, Gemm64, Gemm128 };
+enum class Cfg { M1, M1Long, M2, M2Long, M4, M4Long, M16, M16Long, M32, M64, Gemm64, Gemm128 };
 
 Cfg pick(int64_t M, int64_t K) {
     const bool long_k = K > 3072;
     if (M == 1) return long_k ? Cfg::M1Long : Cfg::M1;
     if (M == 2) return long_k ? Cfg::M2Long : Cfg::M2;
-    if (M <= 4) return Cfg::M4;
-    if (M <= 16) return Cfg::M16;
+    if (M <= 4) return long_k ? Cfg::M4Long : Cfg::M4;
+    if (M <= 16) return long_k ? Cfg::M16Long : Cfg::M16;
     if (M <= 32) return Cfg::M32;
     if (M <= 64) return Cfg::M64;
     return M < 2048 ? Cfg::Gemm64 : Cfg::Gemm128;
+}
+
+// Name of a skinny_kernel instantiation, with the x staging the launch picks.
+const char *skinny_name(int64_t M, int64_t K, int mrows_max, const char *lds_name, const char *l2_name) {
+    return skinny_x_bytes(M, K, mrows_max) <= xlds_budget(mrows_max) ? lds_name : l2_name;
 }
 }  // namespace
 
 const char *linear_config_name(int64_t M, int64_t K) {
     switch (pick(M, K)) {
-        case Cfg::M1: return "skinny_kernel<1, 1, 4, 2, true, 6, false>";
-        case Cfg::M1Long: return "skinny_kernel<1, 1, 8, 3, true, 0, false>";
-        case Cfg::M2: return "skinny_kernel<2, 1, 4, 2, true, 6, false>";
-        case Cfg::M2Long: return "skinny_kernel<2, 1, 8, 3, true, 0, false>";
-        case Cfg::M4: return "skinny_kernel<4, 1, 4, 2, true, 0, false>";
-        case Cfg::M16: return "skinny_kernel<16, 1, 4, 2, true, 0, false>";
+        case Cfg::M1: return skinny_name(M, K, 1, "skinny_kernel<1, 1, 8, 3, true, 6, false>", "skinny_kernel<1, 1, 8, 3, false, 6, false>");
+        case Cfg::M1Long: return skinny_name(M, K, 1, "skinny_kernel<1, 1, 16, 2, true, 0, false>", "skinny_kernel<1, 1, 16, 2, false, 0, false>");
+        case Cfg::M2: return skinny_name(M, K, 2, "skinny_kernel<2, 1, 4, 2, true, 6, false>", "skinny_kernel<2, 1, 4, 2, false, 6, false>");
+        case Cfg::M2Long: return skinny_name(M, K, 2, "skinny_kernel<2, 1, 16, 2, true, 0, false>", "skinny_kernel<2, 1, 16, 2, false, 0, false>");
+        case Cfg::M4: return skinny_name(M, K, 4, "skinny_kernel<4, 1, 4, 2, true, 0, false>", "skinny_kernel<4, 1, 4, 2, false, 0, false>");
+        case Cfg::M4Long: return skinny_name(M, K, 4, "skinny_kernel<4, 1, 16, 2, true, 0, false>", "skinny_kernel<4, 1, 16, 2, false, 0, false>");
+        case Cfg::M16: return skinny_name(M, K, 16, "skinny_kernel<16, 1, 4, 2, true, 0, false>", "skinny_kernel<16, 1, 4, 2, false, 0, false>");
+        case Cfg::M16Long: return skinny_name(M, K, 16, "skinny_kernel<16, 1, 16, 2, true, 0, false>", "skinny_kernel<16, 1, 16, 2, false, 0, false>");
         case Cfg::M32: return "gemm_kernel<2, 1, 1, 8, 0>";
         case Cfg::M64: return "gemm_kernel<4, 1, 1, 8, 0>";
         case Cfg::Gemm64: return "gemm3_kernel<4, 1, 1, 8, 4, 8, false>";
@@ -866,12 +894,14 @@ const char *linear_config_name(int64_t M, int64_t K) {
 
 hipError_t launch_linear(LinearArgs a, hipStream_t s) {
     switch (pick(a.M, a.K)) {
-        case Cfg::M1: return run_skinny<1, 1, 4, 2, 6>(a, s);
-        case Cfg::M1Long: return run_skinny<1, 1, 8, 3, 0>(a, s);
+        case Cfg::M1: return run_skinny<1, 1, 8, 3, 6>(a, s);
+        case Cfg::M1Long: return run_skinny<1, 1, 16, 2, 0>(a, s);
         case Cfg::M2: return run_skinny<2, 1, 4, 2, 6>(a, s);
-        case Cfg::M2Long: return run_skinny<2, 1, 8, 3, 0>(a, s);
+        case Cfg::M2Long: return run_skinny<2, 1, 16, 2, 0>(a, s);
         case Cfg::M4: return run_skinny<4, 1, 4, 2, 0>(a, s);
+        case Cfg::M4Long: return run_skinny<4, 1, 16, 2, 0>(a, s);
         case Cfg::M16: return run_skinny<16, 1, 4, 2, 0>(a, s);
+        case Cfg::M16Long: return run_skinny<16, 1, 16, 2, 0>(a, s);
         case Cfg::M32: return run_gemm<2, 1, 1, 8, 0>(a, s);
         case Cfg::M64: return run_gemm<4, 1, 1, 8, 0>(a, s);
         case Cfg::Gemm64: return run_gemm3<4, 1, 1, 8, 4, 8>(a, s);
@@ -880,16 +910,19 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
 }
 
 // The gated (SwiGLU) launch: the plain configurations with the gate and up
-// rows of a tile on separate waves (skinny: 2 WK waves; gemm3: WN / 2 gate
-// waves and WN / 2 up waves), so every wave runs the plain arithmetic.
+// rows of a tile on separate waves (skinny: 2 WK waves, at most 8 K-slices
+// so a workgroup stays within 1024 threads; gemm3: WN / 2 gate and WN / 2 up
+// waves), so every wave runs the plain arithmetic.
 const char *linear_glu_config_name(int64_t M, int64_t K) {
     switch (pick(M, K)) {
-        case Cfg::M1: return "skinny_kernel<1, 1, 4, 2, true, 6, true>";
-        case Cfg::M1Long: return "skinny_kernel<1, 1, 8, 3, true, 0, true>";
-        case Cfg::M2: return "skinny_kernel<2, 1, 4, 2, true, 6, true>";
-        case Cfg::M2Long: return "skinny_kernel<2, 1, 8, 3, true, 0, true>";
-        case Cfg::M4: return "skinny_kernel<4, 1, 4, 2, true, 0, true>";
-        case Cfg::M16: return "skinny_kernel<16, 1, 4, 2, true, 0, true>";
+        case Cfg::M1: return skinny_name(M, K, 1, "skinny_kernel<1, 1, 8, 3, true, 6, true>", "skinny_kernel<1, 1, 8, 3, false, 6, true>");
+        case Cfg::M1Long: return skinny_name(M, K, 1, "skinny_kernel<1, 1, 8, 3, true, 0, true>", "skinny_kernel<1, 1, 8, 3, false, 0, true>");
+        case Cfg::M2: return skinny_name(M, K, 2, "skinny_kernel<2, 1, 4, 2, true, 6, true>", "skinny_kernel<2, 1, 4, 2, false, 6, true>");
+        case Cfg::M2Long: return skinny_name(M, K, 2, "skinny_kernel<2, 1, 8, 3, true, 0, true>", "skinny_kernel<2, 1, 8, 3, false, 0, true>");
+        case Cfg::M4: return skinny_name(M, K, 4, "skinny_kernel<4, 1, 4, 2, true, 0, true>", "skinny_kernel<4, 1, 4, 2, false, 0, true>");
+        case Cfg::M4Long: return skinny_name(M, K, 4, "skinny_kernel<4, 1, 8, 3, true, 0, true>", "skinny_kernel<4, 1, 8, 3, false, 0, true>");
+        case Cfg::M16: return skinny_name(M, K, 16, "skinny_kernel<16, 1, 4, 2, true, 0, true>", "skinny_kernel<16, 1, 4, 2, false, 0, true>");
+        case Cfg::M16Long: return skinny_name(M, K, 16, "skinny_kernel<16, 1, 8, 3, true, 0, true>", "skinny_kernel<16, 1, 8, 3, false, 0, true>");
         case Cfg::M32: return "gemm3_kernel<2, 1, 1, 8, 0, 8, true>";
         case Cfg::M64: return "gemm3_kernel<4, 1, 1, 8, 0, 8, true>";
         case Cfg::Gemm64: return "gemm3_kernel<4, 1, 1, 8, 4, 8, true>";
@@ -899,12 +932,14 @@ const char *linear_glu_config_name(int64_t M, int64_t K) {
 
 hipError_t launch_linear_glu(LinearArgs a, hipStream_t s) {
     switch (pick(a.M, a.K)) {
-        case Cfg::M1: return run_skinny<1, 1, 4, 2, 6, true>(a, s);
+        case Cfg::M1: return run_skinny<1, 1, 8, 3, 6, true>(a, s);
         case Cfg::M1Long: return run_skinny<1, 1, 8, 3, 0, true>(a, s);
         case Cfg::M2: return run_skinny<2, 1, 4, 2, 6, true>(a, s);
         case Cfg::M2Long: return run_skinny<2, 1, 8, 3, 0, true>(a, s);
         case Cfg::M4: return run_skinny<4, 1, 4, 2, 0, true>(a, s);
+        case Cfg::M4Long: return run_skinny<4, 1, 8, 3, 0, true>(a, s);
         case Cfg::M16: return run_skinny<16, 1, 4, 2, 0, true>(a, s);
+        case Cfg::M16Long: return run_skinny<16, 1, 8, 3, 0, true>(a, s);
         case Cfg::M32: return run_gemm3<2, 1, 1, 8, 0, 8, true>(a, s);
         case Cfg::M64: return run_gemm3<4, 1, 1, 8, 0, 8, true>(a, s);
         case Cfg::Gemm64: return run_gemm3<4, 1, 1, 8, 4, 8, true>(a, s);
