@@ -915,7 +915,7 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
 // waves), so every wave runs the plain arithmetic.
 const char *linear_glu_config_name(int64_t M, int64_t K) {
     switch (pick(M, K)) {
-        case Cfg::M1: return skinny_name(M, K, 1, "skinny_kernel<1, 1, 8, 3, true, 6, true>", "skinny_kernel<1, 1, 8, 3, false, 6, true>");
+        case Cfg::M1: return skinny_name(M, K, 1, "skinny_kernel<1, 1, 4, 2, true, 6, true>", "skinny_kernel<1, 1, 4, 2, false, 6, true>");
         case Cfg::M1Long: return skinny_name(M, K, 1, "skinny_kernel<1, 1, 8, 3, true, 0, true>", "skinny_kernel<1, 1, 8, 3, false, 0, true>");
         case Cfg::M2: return skinny_name(M, K, 2, "skinny_kernel<2, 1, 4, 2, true, 6, true>", "skinny_kernel<2, 1, 4, 2, false, 6, true>");
         case Cfg::M2Long: return skinny_name(M, K, 2, "skinny_kernel<2, 1, 8, 3, true, 0, true>", "skinny_kernel<2, 1, 8, 3, false, 0, true>");
@@ -932,7 +932,7 @@ const char *linear_glu_config_name(int64_t M, int64_t K) {
 
 hipError_t launch_linear_glu(LinearArgs a, hipStream_t s) {
     switch (pick(a.M, a.K)) {
-        case Cfg::M1: return run_skinny<1, 1, 8, 3, 6, true>(a, s);
+        case Cfg::M1: return run_skinny<1, 1, 4, 2, 6, true>(a, s);
         case Cfg::M1Long: return run_skinny<1, 1, 8, 3, 0, true>(a, s);
         case Cfg::M2: return run_skinny<2, 1, 4, 2, 6, true>(a, s);
         case Cfg::M2Long: return run_skinny<2, 1, 8, 3, 0, true>(a, s);
