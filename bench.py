@@ -338,7 +338,7 @@ def time_lm_head(spec, pw, ms, reps, dev):
         torch.cuda.synchronize(dev)
         t = float(np.median([a.elapsed_time(b) / 1e3 for a, b in pairs]))
         moved = algorithmic_bytes(spec, m)
-        out[f"M={m}"] = {"kernel": q4.linear_kernel(m, spec.K), "us": round(t * 1e6, 2),
+        out[f"M={m}"] = {"kernel": q4.linear_kernel(m, spec.K, spec.Ns), "us": round(t * 1e6, 2),
                          "GBs": round(moved / t / 1e9, 1), "frac_of_8TBs": round(moved / t / 1e9 / HBM_PEAK_GBS, 4),
                          "TFLOPs": round(flops(spec, m) / t / 1e12, 2), "launches": reps}
     del flush, sink
@@ -445,7 +445,7 @@ def main():
     by_kernel = collections.OrderedDict()
     per_op = collections.OrderedDict()
     for (spec, *_), d in zip(runner.items, durations):
-        kname = q4.linear_kernel(1, spec.K)
+        kname = q4.linear_kernel(1, spec.K, spec.Ns)
         b, t, c = by_kernel.get(kname, (0, 0.0, 0))
         by_kernel[kname] = (b + algorithmic_bytes(spec, 1) * len(d), t + sum(d), c + len(d))
         op = spec.name.split(".", 1)[1]
@@ -517,6 +517,12 @@ def main():
         pk_time = sum(sum(d) for d in pdur)
         pk_flops = sum(flops(spec, 2048) * len(d) for (spec, *_), d in zip(prunner.items, pdur))
         pach = pk_flops / pk_time / 1e12
+        # the GEMM tile shape depends on the shape's work tiles: name the one
+        # holding the most kernel time, and every op's
+        pk_names = [q4.linear_kernel(2048, spec.K, spec.Ns) for spec, *_ in prunner.items]
+        pk_by = collections.Counter()
+        for name, d in zip(pk_names, pdur):
+            pk_by[name] += sum(d)
         out["prefill"] = {
             "value": round(tflops, 2),
             "unit": "TFLOP/s",
@@ -525,7 +531,8 @@ def main():
             "steps": args.prefill_steps,
             "roofline": {
                 "bound": "mfma",
-                "kernel": q4.linear_kernel(2048, 3072),
+                "kernel": pk_by.most_common(1)[0][0],
+                "kernels": {spec.name.split(".", 1)[1]: name for (spec, *_), name in zip(prunner.items, pk_names)},
                 "achieved": round(pach, 2),
                 "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s",

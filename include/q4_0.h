@@ -176,12 +176,17 @@ q4_status q4_0_linear_swiglu(const void *x_bf16, int64_t M, int64_t K, const voi
 const char *q4_0_linear_swiglu_kernel(int64_t M, int64_t K);
 
 /*
- * Name of the kernel instantiation q4_0_linear runs for this M and K (the
- * configuration depends on M and K only, never on N, so a fused launch and
- * separate launches of its segments run the same arithmetic).  Static string;
- * "" for an invalid M or K.  For reports that match timings to kernel names.
+ * Name of the kernel instantiation q4_0_linear_multi runs for M, K and the
+ * segments' row counts N[0 .. nseg-1] (host array; q4_0_linear is nseg = 1).
+ * Up to 64 rows the configuration depends on M and K only; above, the GEMM
+ * tile shape also depends on how many work tiles the segments make and on the
+ * current device's compute-unit count (256 is assumed when no device answers).
+ * The tile shapes add the block results of an output in the same order, so a
+ * fused launch and separate launches of its segments give bitwise equal
+ * results whichever shapes they run.  Static string; "" for an invalid
+ * argument.  For reports that match timings to kernel names.
  */
-const char *q4_0_linear_kernel(int64_t M, int64_t K);
+const char *q4_0_linear_kernel(int64_t M, int64_t K, const int64_t *N, int nseg);
 
 /*
  * Measurement hook for benchmarks.  Arms the calling thread's next

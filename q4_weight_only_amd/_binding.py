@@ -68,7 +68,7 @@ def lib() -> ctypes.CDLL:
             L.q4_0_linear.restype = i32
             L.q4_0_linear_multi.argtypes = [vp, i64, i64, ctypes.POINTER(Segment), i32, vp]
             L.q4_0_linear_multi.restype = i32
-            L.q4_0_linear_kernel.argtypes = [i64, i64]
+            L.q4_0_linear_kernel.argtypes = [i64, i64, ctypes.POINTER(i64), i32]
             L.q4_0_linear_kernel.restype = ctypes.c_char_p
             L.q4_0_linear_swiglu.argtypes = [vp, i64, i64, vp, vp, i64, vp, i32, vp]
             L.q4_0_linear_swiglu.restype = i32
@@ -262,9 +262,12 @@ def time_next_launch(start: "torch.cuda.Event", stop: "torch.cuda.Event") -> Non
     _check(lib().q4_0_time_next_launch(start.cuda_event, stop.cuda_event), "q4_0_time_next_launch")
 
 
-def linear_kernel(m: int, k: int) -> str:
-    """Name of the kernel q4_0_linear runs for (M, K)."""
-    return lib().q4_0_linear_kernel(int(m), int(k)).decode()
+def linear_kernel(m: int, k: int, n) -> str:
+    """Name of the kernel q4_0_linear_multi runs for (M, K) over segments of
+    n rows (an int for a single q4_0_linear, or a sequence of segment rows)."""
+    ns = [int(n)] if isinstance(n, int) else [int(v) for v in n]
+    arr = (ctypes.c_int64 * max(len(ns), 1))(*ns)
+    return lib().q4_0_linear_kernel(int(m), int(k), arr, len(ns)).decode()
 
 
 def linear_swiglu_kernel(m: int, k: int) -> str:

@@ -156,9 +156,22 @@ const char *q4_0_linear_swiglu_kernel(int64_t M, int64_t K) {
     return q4::linear_glu_config_name(M, K);
 }
 
-const char *q4_0_linear_kernel(int64_t M, int64_t K) {
-    if (M < 1 || M > kMaxM || !shape_ok(1, K)) return "";
-    return q4::linear_config_name(M, K);
+const char *q4_0_linear_kernel(int64_t M, int64_t K, const int64_t *N, int nseg) {
+    if (!N || nseg < 1 || nseg > q4::kMaxSegments || M < 1 || M > kMaxM) return "";
+    q4::LinearArgs a;
+    a.x = nullptr;
+    a.M = static_cast<int32_t>(M);
+    a.K = static_cast<int32_t>(K);
+    a.nseg = nseg;
+    a.y_bf16 = 0;
+    for (int i = 0; i < q4::kMaxSegments; ++i) a.seg[i] = q4::Segment{};
+    for (int i = 0; i < nseg; ++i) {
+        if (!shape_ok(N[i], K)) return "";
+        a.seg[i].N = static_cast<int32_t>(N[i]);
+        a.seg[i].RT = static_cast<int32_t>(q4::PackedDims(N[i], K).RT);
+    }
+    a.KT = static_cast<int32_t>(q4::round_up(K, q4::kTileK) / q4::kTileK);
+    return q4::linear_config_name(a);
 }
 
 q4_status q4_0_time_next_launch(void *start_event, void *stop_event) {

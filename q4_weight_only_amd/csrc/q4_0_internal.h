@@ -60,9 +60,9 @@ hipError_t launch_embed(const uint8_t *packed, int64_t N, int64_t K, const int32
 // filled in by the launcher).
 hipError_t launch_linear(LinearArgs a, hipStream_t s);
 
-// Name of the kernel instantiation launch_linear picks for (M, K); the
-// XLDS flag in it is the choice when x fits in LDS.
-const char *linear_config_name(int64_t M, int64_t K);
+// Name of the kernel instantiation launch_linear picks for a launch (M, K
+// and, above 64 rows, the segments' RT and the current device's CU count).
+const char *linear_config_name(const LinearArgs &a);
 
 // The gated launch: segment 0 is gate (its y receives silu(gate) * up),
 // segment 1 is up, of the same shape; tile_begin is filled in here too.

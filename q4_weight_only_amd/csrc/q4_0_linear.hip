@@ -850,15 +850,29 @@ void arm_launch_events(hipEvent_t start, hipEvent_t stop) {
     t_stop_event = stop;
 }
 
-// The dispatch table: kernel configuration by M and K.  Decode sizes split K
-// over the waves of a workgroup with a short prefetch, so that many waves
-// stay resident (the launches are latency-bound); long rows (K > 3072) split
-// K wider.  Above 64 rows the GEMM takes 64-row tiles below 2048 rows (more
-// workgroups for the 1.5k-row audio shapes) and 128-row tiles from there on.
+// The dispatch table.  Decode sizes (M <= 64) pick by M and K: skinny
+// kernels split K over the waves of a workgroup with a short prefetch, so
+// that many waves stay resident (the launches are latency-bound); long rows
+// (K > 3072) split K wider.  Above 64 rows three GEMM tile shapes compete on
+// how evenly their work tiles spread over the device's compute units:
+//   gemm3 64 x 128   (two workgroups per CU),
+//   gemm3 128 x 128  (two workgroups per CU),
+//   gemm3 128 x 192  (12 waves, one workgroup per CU).
+// A launch costs about ceil(tiles / CUs) x the time of one tile on a fully
+// occupied CU; measured on MI355X at M = 1505, 2048 and 6020 over the decoder,
+// adapter and encoder shapes, those per-tile times are 0.30 : 0.50 : 0.85
+// (the 128-row tiles' unit), and the smallest estimate wins (a tie goes to
+// 128 x 128, then to 64 x 128).  This puts N = 3072 at
+// M = 2048 (384 tiles of 128 x 128 on 256 CUs, a last round half empty) on
+// exactly 256 tiles of 128 x 192.  Every GEMM tile shape adds the block
+// results of an output in the same order, so the choice never changes a
+// result.
 namespace {
-enum class Cfg { M1, M1Long, M2, M2Long, M4, M4Long, M16, M16Long, M32, M64, Gemm64, Gemm128 };
+enum class Cfg { M1, M1Long, M2, M2Long, M4, M4Long, M16, M16Long, M32, M64, Gemm64, Gemm128, Gemm128W };
 
-Cfg pick(int64_t M, int64_t K) {
+// Configuration by M and K alone: the decode sizes, and the gated launch's
+// GEMM split at 2048 rows.
+Cfg pick_mk(int64_t M, int64_t K) {
     const bool long_k = K > 3072;
     if (M == 1) return long_k ? Cfg::M1Long : Cfg::M1;
     if (M == 2) return long_k ? Cfg::M2Long : Cfg::M2;
@@ -869,14 +883,51 @@ Cfg pick(int64_t M, int64_t K) {
     return M < 2048 ? Cfg::Gemm64 : Cfg::Gemm128;
 }
 
+// Compute units of the current device, queried once per device (256 on
+// MI355X; also the answer when there is no device to ask).
+int device_cus() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        n = 256;
+    }
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Work tiles of a BM x BN GEMM tiling over all segments of a launch.
+int64_t gemm_tiles(const LinearArgs &a, int bm, int bn) {
+    const int rows_per_tile = bn / kTileRows;
+    int64_t ntiles = 0;
+    for (int i = 0; i < a.nseg; ++i) ntiles += (a.seg[i].RT + rows_per_tile - 1) / rows_per_tile;
+    return ntiles * ((a.M + bm - 1) / bm);
+}
+
+Cfg pick(const LinearArgs &a) {
+    if (a.M <= 64) return pick_mk(a.M, a.K);
+    const int64_t cus = device_cus();
+    auto cost = [&](int bm, int bn, int64_t unit) { return (gemm_tiles(a, bm, bn) + cus - 1) / cus * unit; };
+    const int64_t c64 = cost(64, 128, 30), c128 = cost(128, 128, 50), c128w = cost(128, 192, 85);
+    if (c128 <= c64 && c128 <= c128w) return Cfg::Gemm128;
+    return c64 <= c128w ? Cfg::Gemm64 : Cfg::Gemm128W;
+}
+
 // Name of a skinny_kernel instantiation, with the x staging the launch picks.
 const char *skinny_name(int64_t M, int64_t K, int mrows_max, const char *lds_name, const char *l2_name) {
     return skinny_x_bytes(M, K, mrows_max) <= xlds_budget(mrows_max) ? lds_name : l2_name;
 }
 }  // namespace
 
-const char *linear_config_name(int64_t M, int64_t K) {
-    switch (pick(M, K)) {
+const char *linear_config_name(const LinearArgs &a) {
+    const int64_t M = a.M, K = a.K;
+    switch (pick(a)) {
         case Cfg::M1: return skinny_name(M, K, 1, "skinny_kernel<1, 1, 8, 3, true, 6, false>", "skinny_kernel<1, 1, 8, 3, false, 6, false>");
         case Cfg::M1Long: return skinny_name(M, K, 1, "skinny_kernel<1, 1, 16, 2, true, 0, false>", "skinny_kernel<1, 1, 16, 2, false, 0, false>");
         case Cfg::M2: return skinny_name(M, K, 2, "skinny_kernel<2, 1, 4, 2, true, 6, false>", "skinny_kernel<2, 1, 4, 2, false, 6, false>");
@@ -888,12 +939,13 @@ const char *linear_config_name(int64_t M, int64_t K) {
         case Cfg::M32: return "gemm_kernel<2, 1, 1, 8, 0>";
         case Cfg::M64: return "gemm_kernel<4, 1, 1, 8, 0>";
         case Cfg::Gemm64: return "gemm3_kernel<4, 1, 1, 8, 4, 8, false>";
+        case Cfg::Gemm128W: return "gemm3_kernel<8, 1, 1, 12, 0, 8, false>";
         default: return "gemm3_kernel<8, 1, 1, 8, 4, 8, false>";
     }
 }
 
 hipError_t launch_linear(LinearArgs a, hipStream_t s) {
-    switch (pick(a.M, a.K)) {
+    switch (pick(a)) {
         case Cfg::M1: return run_skinny<1, 1, 8, 3, 6>(a, s);
         case Cfg::M1Long: return run_skinny<1, 1, 16, 2, 0>(a, s);
         case Cfg::M2: return run_skinny<2, 1, 4, 2, 6>(a, s);
@@ -905,6 +957,7 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
         case Cfg::M32: return run_gemm<2, 1, 1, 8, 0>(a, s);
         case Cfg::M64: return run_gemm<4, 1, 1, 8, 0>(a, s);
         case Cfg::Gemm64: return run_gemm3<4, 1, 1, 8, 4, 8>(a, s);
+        case Cfg::Gemm128W: return run_gemm3<8, 1, 1, 12, 0, 8>(a, s);
         default: return run_gemm3<8, 1, 1, 8, 4, 8>(a, s);
     }
 }
@@ -914,7 +967,7 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
 // so a workgroup stays within 1024 threads; gemm3: WN / 2 gate and WN / 2 up
 // waves), so every wave runs the plain arithmetic.
 const char *linear_glu_config_name(int64_t M, int64_t K) {
-    switch (pick(M, K)) {
+    switch (pick_mk(M, K)) {
         case Cfg::M1: return skinny_name(M, K, 1, "skinny_kernel<1, 1, 4, 2, true, 6, true>", "skinny_kernel<1, 1, 4, 2, false, 6, true>");
         case Cfg::M1Long: return skinny_name(M, K, 1, "skinny_kernel<1, 1, 8, 3, true, 0, true>", "skinny_kernel<1, 1, 8, 3, false, 0, true>");
         case Cfg::M2: return skinny_name(M, K, 2, "skinny_kernel<2, 1, 4, 2, true, 6, true>", "skinny_kernel<2, 1, 4, 2, false, 6, true>");
@@ -931,7 +984,7 @@ const char *linear_glu_config_name(int64_t M, int64_t K) {
 }
 
 hipError_t launch_linear_glu(LinearArgs a, hipStream_t s) {
-    switch (pick(a.M, a.K)) {
+    switch (pick_mk(a.M, a.K)) {
         case Cfg::M1: return run_skinny<1, 1, 4, 2, 6, true>(a, s);
         case Cfg::M1Long: return run_skinny<1, 1, 8, 3, 0, true>(a, s);
         case Cfg::M2: return run_skinny<2, 1, 4, 2, 6, true>(a, s);

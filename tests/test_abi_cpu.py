@@ -126,6 +126,32 @@ def test_linear_swiglu_validates_first(L):
     assert b"true" in L.q4_0_linear_swiglu_kernel(1, 3072)        # the gated instantiation
 
 
+def test_linear_kernel_names(L):
+    """The kernel-name query is host logic: invalid arguments give "", decode
+    sizes name a skinny kernel, and above 64 rows the GEMM tile shape follows
+    the launch's tile count (256 compute units are assumed without a device)."""
+    import ctypes
+    kn = L.q4_0_linear_kernel
+
+    def arr(*ns):
+        return (ctypes.c_int64 * len(ns))(*ns)
+    assert kn(0, 64, arr(16), 1) == b""
+    assert kn(1, 48, arr(16), 1) == b""                 # K % 32
+    assert kn(1, 64, arr(0), 1) == b""                  # N < 1
+    assert kn(1, 64, arr(16), 0) == b""                 # no segment
+    assert kn(1, 64, arr(*([16] * 9)), 9) == b""        # too many segments
+    assert kn(1, 64, None, 1) == b""
+    assert kn(1, 3072, arr(4096, 1024, 1024), 3).startswith(b"skinny_kernel<1, ")
+    assert kn(20, 3072, arr(3072), 1) == b"gemm_kernel<2, 1, 1, 8, 0>"
+    assert kn(40, 3072, arr(3072), 1) == b"gemm_kernel<4, 1, 1, 8, 0>"
+    import torch
+    if torch.cuda.is_available() and torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        return                                          # the tile counts below assume 256 CUs
+    assert kn(2048, 4096, arr(3072), 1) == b"gemm3_kernel<8, 1, 1, 12, 0, 8, false>"
+    assert kn(2048, 3072, arr(3072, 3072, 3072), 3) == b"gemm3_kernel<8, 1, 1, 8, 4, 8, false>"
+    assert kn(300, 3072, arr(3072), 1) == b"gemm3_kernel<4, 1, 1, 8, 4, 8, false>"
+
+
 def test_embed_validates_first(L):
     em = L.q4_0_embed
     assert em(FAKE, 16, 48, FAKE, 4, FAKE, None) == SHAPE          # K % 32

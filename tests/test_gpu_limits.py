@@ -28,7 +28,7 @@ def test_limit_shapes_every_output(m, n, k):
     x = inputs.activations_bf16((m, k), seed=61, tags=(m, k))
     pw, blocks = device_weight_from_f32(w)
     b = blocks.cpu().numpy()
-    say("limits", m, n, k, q4.linear_kernel(m, k))
+    say("limits", m, n, k, q4.linear_kernel(m, k, n))
     y = q4.linear(to_dev_x(x), pw).cpu().numpy()
     assert_within_bound(y, O.linear(x, b, n, k), O.error_bound(x, b, n, k), f"M={m} N={n} K={k}")
 
@@ -38,7 +38,7 @@ def test_limit_rows_sampled(m, n, k):
     w = inputs.weights_f32((n, k), seed=62, tags=(n, k))
     x = inputs.activations_bf16((m, k), seed=62, tags=(m, k))
     pw, blocks = device_weight_from_f32(w)
-    say("limits rows", m, n, k, q4.linear_kernel(m, k))
+    say("limits rows", m, n, k, q4.linear_kernel(m, k, n))
     y = q4.linear(to_dev_x(x), pw).cpu().numpy()
     rows = sample_rows(n, 256, 62)
     b = blocks.cpu().numpy().reshape(n, -1)[rows]
