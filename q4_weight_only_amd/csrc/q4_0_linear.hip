@@ -521,10 +521,16 @@ struct Gemm3Cfg {
     static constexpr int BN = 16 * NT * WN;
     static constexpr int kThreads = 64 * WM * WN;
     static constexpr int kAStep = BM * 16 / kTileBlocks;   // 16-byte x chunks staged per block step
-    // Threads per staged chunk set: all threads, or kAStep of them for a small
-    // tile; the other waves then load and store the same chunks again (the
-    // same bytes to the same place), which keeps the loop free of branches.
-    static constexpr int kStagers = kAStep < kThreads ? kAStep : kThreads;
+    // Threads per staged chunk set: the largest whole number of waves that
+    // divides the chunks of a step (all threads when they do); the other
+    // waves then load and store the same chunks again (the same bytes to the
+    // same place), which keeps the loop free of branches.
+    static constexpr int stagers() {
+        int t = kThreads < kAStep ? kThreads : kAStep;
+        while (t > 64 && kAStep % t != 0) t -= 64;
+        return t;
+    }
+    static constexpr int kStagers = stagers();
     static constexpr int kAPerThread = kAStep / kStagers;
     static_assert(kAStep % kStagers == 0 && kStagers % 64 == 0, "x staging must split evenly over whole waves");
 };
@@ -570,28 +576,24 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
     const int KT = a.KT;
     const int nblk = a.K / kQK;
 
-    // ---- x staging: part p of a tile is chunks p * kAStep + tid % kStagers + kStagers * j.
-    // Loads go through a buffer resource over this tile's rows, so a chunk
-    // past K gets an offset beyond the resource's size and reads zeros, with
-    // no branch.  Rows past M read row M - 1 (their outputs are never stored).
+    // ---- x staging: part p of a tile is chunks p * kAStep + tid % kStagers + kStagers * j,
+    // i.e. chunk c = tid % 16 of rows p * kAStep / 16 + (tid % kStagers) / 16 + j * kStagers / 16
+    // (both steps are multiples of 16 rows, so every chunk of a thread has the same c).
+    // Loads go through a buffer resource over this tile's rows: a row past M
+    // lies beyond the resource's size and reads zeros (its outputs are never
+    // stored), and a chunk past K gets an offset beyond every resource, so
+    // the loop has no branch.
     const int rows = a.M - m0 < BM ? a.M - m0 : BM;
     const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.x + static_cast<int64_t>(m0) * a.K), 0, rows * a.K * 2, kBufferRsrcWord3);
-    int x_off[kTileBlocks][NPT];   // byte offset in the tile's rows at k-step 0
-    int x_kt_end[kTileBlocks][NPT];   // first k-step whose chunk lies past K
-#pragma unroll
-    for (int p = 0; p < kTileBlocks; ++p)
-#pragma unroll
-        for (int j = 0; j < NPT; ++j) {
-            const int qc = p * C::kAStep + tid % C::kStagers + C::kStagers * j;
-            const int m = qc >> 4, c = qc & 15;
-            x_off[p][j] = (m < rows ? m : rows - 1) * a.K * 2 + c * 16;
-            x_kt_end[p][j] = (nblk - (c >> 2) + kTileBlocks - 1) / kTileBlocks;
-        }
+    const int x_st = tid % C::kStagers, x_c = x_st & 15;
+    const int x_base = (x_st >> 4) * a.K * 2 + x_c * 16;                  // byte offset at k-step 0, part 0, j 0
+    const int x_kt_end = (nblk - (x_c >> 2) + kTileBlocks - 1) / kTileBlocks;   // first k-step past K
     auto load_part = [&](u32x4 (&R)[NPT], int kt, int part) {
 #pragma unroll
         for (int j = 0; j < NPT; ++j) {
-            const int off = kt < x_kt_end[part][j] ? x_off[part][j] : kOutOfRange;
+            const int row = part * (C::kAStep / 16) + j * (C::kStagers / 16);
+            const int off = kt < x_kt_end ? x_base + row * a.K * 2 : kOutOfRange;
             R[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, off, kt * kTileK * 2, 0));
         }
     };
@@ -604,16 +606,20 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
         }
     };
 
-    // ---- weights: this wave's NT tiles, straight into registers
-    const uint8_t *nib_base[NT];
-    const uint16_t *sc_base[NT];
+    // ---- weights: this wave's NT tiles, straight into registers.  Each tile
+    // row's planes are a buffer resource (wave-uniform, in SGPRs) read at a
+    // per-lane offset shared by all tiles, so the addresses cost no VGPRs.
+    __amdgpu_buffer_rsrc_t nib_rsrc[NT], sc_rsrc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int rt = rt_base + nt < src.RT ? rt_base + nt : src.RT - 1;
         const int64_t T0 = static_cast<int64_t>(rt) * KT;
-        nib_base[nt] = src.nib + T0 * kTileNibBytes + lane * 16;
-        sc_base[nt] = src.scales + T0 * kTileScales + nl * 4;
+        nib_rsrc[nt] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(src.nib + T0 * kTileNibBytes), 0,
+                                                         KT * kTileNibBytes, kBufferRsrcWord3);
+        sc_rsrc[nt] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(src.scales + T0 * kTileScales), 0,
+                                                        KT * kTileScales * 2, kBufferRsrcWord3);
     }
+    const int nib_lane = lane * 16, sc_lane = nl * 8;
     struct BStage {
         u32x4 nib[NT];
         u32x2 sc[NT];
@@ -621,8 +627,8 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
     auto load_b = [&](BStage &S, int kt) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            S.nib[nt] = *reinterpret_cast<const u32x4 *>(nib_base[nt] + static_cast<int64_t>(kt) * kTileNibBytes);
-            S.sc[nt] = *reinterpret_cast<const u32x2 *>(sc_base[nt] + static_cast<int64_t>(kt) * kTileScales);
+            S.nib[nt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(nib_rsrc[nt], nib_lane, kt * kTileNibBytes, 0));
+            S.sc[nt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(sc_rsrc[nt], sc_lane, kt * kTileScales * 2, 0));
         }
     };
 
