@@ -20,9 +20,11 @@ Printed (one JSON line):
               and the GEMM kernel's roofline against 2.5 PFLOP/s bf16
   swiglu      the fused gate/up + SwiGLU launch (q4_0_linear_swiglu) next to
               the unfused gate/up launch it replaces, at M = 1, 2 and 2048
-              (kernel-own times over the 26 layers' gate/up weights)
+              (kernel-own times; each kind walks the 26 layers' gate/up
+              weights in turn, so every launch streams its weights from HBM)
   embed       Q4 embedding lookups (q4_0_embed) of 32, 2048 and 16384 random ids
-              from the 131072 x 3072 table: time per launch and GB/s moved
+              from the 131072 x 3072 table: kernel-own time per launch, each
+              after a 512 MiB read (rows from HBM), and GB/s moved
   lm_head     the same table as the LM head linear at M = 1 and 32 (kernel-own
               times, each launch after a 512 MiB read so the table comes from HBM)
   cpu_baseline  the CPU oracle (dequantize + fp64 matmul) on a bounded sample
@@ -214,7 +216,9 @@ def time_kernels(runner, steps, dev):
 def time_swiglu(prepared, ms, reps, dev):
     """Kernel-own times of the fused gate/up + SwiGLU launch next to the
     unfused gate/up launch it replaces, over the decode workload's gate/up
-    weights (one per layer, rotated so the weights stream from HBM)."""
+    weights.  Each kind of launch walks all layers' weight pairs in turn, so
+    25 other pairs (800 MB) stream through between two uses of one pair and
+    every launch reads its weights from HBM, not from the infinity cache."""
     import numpy as np
     import torch
 
@@ -233,8 +237,8 @@ def time_swiglu(prepared, ms, reps, dev):
         ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for _ in range(2)]
         pairs = {"fused": [], "fused_bf16": [], "unfused": []}
         for r in range(reps + 1):
-            for _, pws in gate_up:
-                for kind in ("fused", "fused_bf16", "unfused"):
+            for kind in ("fused", "fused_bf16", "unfused"):
+                for _, pws in gate_up:
                     a = torch.cuda.Event(enable_timing=True)
                     b = torch.cuda.Event(enable_timing=True)
                     a.record(stream)
@@ -269,40 +273,39 @@ def time_swiglu(prepared, ms, reps, dev):
 
 
 def time_embed(pw, counts, reps, dev):
-    """Q4 embedding lookups from the packed table: `reps` launches captured in
-    one HIP graph, replayed and timed with HIP events (so host launch cost
-    does not count), for each batch size."""
+    """Kernel-own times (armed events) of Q4 embedding lookups, each launch
+    with fresh random ids and after a read of a 512 MiB buffer, so the table
+    rows come from HBM: the 226 MB table would otherwise sit in the 256 MB
+    infinity cache after the first launches."""
     import numpy as np
     import torch
 
     import q4_weight_only_amd as q4
 
     rng = np.random.default_rng(7)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
     out = {}
-    stream = torch.cuda.Stream(dev)
     for count in counts:
-        ids = torch.from_numpy(rng.integers(0, pw.n, count).astype(np.int32)).to(dev)
+        ids = [torch.from_numpy(rng.integers(0, pw.n, count).astype(np.int32)).to(dev) for _ in range(reps + 1)]
         res = torch.empty((count, pw.k), dtype=torch.float32, device=dev)
-        stream.wait_stream(torch.cuda.current_stream(dev))
-        with torch.cuda.stream(stream):
-            q4.embed(pw, ids, res)
-        torch.cuda.synchronize(dev)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for _ in range(reps):
-                q4.embed(pw, ids, res)
-        with torch.cuda.stream(stream):
-            graph.replay()
+        pairs = []
+        for r, batch in enumerate(ids):
+            torch.sum(flush, dim=0, out=sink)
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            graph.replay()
             b.record(stream)
-        b.synchronize()
-        del graph
-        t = a.elapsed_time(b) / 1e3 / reps
+            q4.time_next_launch(a, b)
+            q4.embed(pw, batch, res)
+            if r > 0:                      # the first launch warms up
+                pairs.append((a, b))
+        torch.cuda.synchronize(dev)
+        t = float(np.median([a.elapsed_time(b) / 1e3 for a, b in pairs]))
         moved = count * (pw.k // 32 * 18 + pw.k * 4 + 4)     # table rows read + fp32 rows written + ids
         out[f"ids={count}"] = {"us": round(t * 1e6, 2), "GBs": round(moved / t / 1e9, 1), "bytes": moved}
+    del flush, sink
     return out
 
 

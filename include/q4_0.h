@@ -190,7 +190,7 @@ const char *q4_0_linear_kernel(int64_t M, int64_t K, const int64_t *N, int nseg)
 
 /*
  * Measurement hook for benchmarks.  Arms the calling thread's next
- * q4_0_linear / q4_0_linear_multi / q4_0_linear_swiglu launch so that its kernel records
+ * q4_0_linear / q4_0_linear_multi / q4_0_linear_swiglu / q4_0_embed launch so that its kernel records
  * `start_event` when it starts executing and `stop_event` when it finishes
  * (hipExtLaunchKernelGGL); hipEventElapsedTime on the pair is then that
  * kernel's own duration, without launch gaps -- the quantity a kernel trace

@@ -257,8 +257,9 @@ def linear_swiglu(x: torch.Tensor, gate: PackedWeight, up: PackedWeight,
 
 
 def time_next_launch(start: "torch.cuda.Event", stop: "torch.cuda.Event") -> None:
-    """Arm this thread's next linear launch to record start/stop at its kernel's
-    own start and end (events must already exist: record them once first)."""
+    """Arm this thread's next linear, SwiGLU or embedding launch to record
+    start/stop at its kernel's own start and end (events must already exist:
+    record them once first)."""
     _check(lib().q4_0_time_next_launch(start.cuda_event, stop.cuda_event), "q4_0_time_next_launch")
 
 

@@ -10,6 +10,8 @@
 
 #include <hip/hip_fp16.h>
 
+#include <hip/hip_ext.h>
+
 #include "q4_0_internal.h"
 
 namespace q4 {
@@ -284,9 +286,14 @@ hipError_t launch_embed(const uint8_t *packed, int64_t N, int64_t K, const int32
     // enough workgroups to fill the chip several times over; the kernel loops
     const int64_t want = (total + kThreads - 1) / kThreads;
     const dim3 grid(static_cast<uint32_t>(want < 65536 ? want : 65536));
-    hipLaunchKernelGGL(embed_kernel, grid, dim3(kThreads), 0, s, packed,
-                       reinterpret_cast<const uint16_t *>(packed + pd.nib_bytes()), (int32_t)N,
-                       (int32_t)K, (int32_t)pd.KT, ids, total, out);
+    const uint16_t *scales = reinterpret_cast<const uint16_t *>(packed + pd.nib_bytes());
+    hipEvent_t start = nullptr, stop = nullptr;
+    if (take_launch_events(start, stop))
+        hipExtLaunchKernelGGL(embed_kernel, grid, dim3(kThreads), 0, s, start, stop, 0, packed, scales, (int32_t)N,
+                              (int32_t)K, (int32_t)pd.KT, ids, total, out);
+    else
+        hipLaunchKernelGGL(embed_kernel, grid, dim3(kThreads), 0, s, packed, scales, (int32_t)N, (int32_t)K,
+                           (int32_t)pd.KT, ids, total, out);
     return hipGetLastError();
 }
 

@@ -69,8 +69,10 @@ const char *linear_config_name(const LinearArgs &a);
 hipError_t launch_linear_glu(LinearArgs a, hipStream_t s);
 const char *linear_glu_config_name(int64_t M, int64_t K);
 
-// Makes the calling thread's next launch_linear record `start` / `stop` at
-// its kernel's start and end.
+// Makes the calling thread's next linear, gated or embedding launch record
+// `start` / `stop` at its kernel's start and end.
 void arm_launch_events(hipEvent_t start, hipEvent_t stop);
+// Takes (and disarms) the calling thread's armed events; false if none.
+bool take_launch_events(hipEvent_t &start, hipEvent_t &stop);
 
 }  // namespace q4

@@ -185,8 +185,8 @@ void skinny_kernel(const LinearArgs a) {
     auto load_w = [&](WStage &S, int j) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            S.nib[nt] = *reinterpret_cast<const u32x4 *>(nib_base[nt] + static_cast<int64_t>(j) * WK * kTileNibBytes);
-            S.sc[nt] = *reinterpret_cast<const u32x2 *>(sc_base[nt] + static_cast<int64_t>(j) * WK * kTileScales);
+            S.nib[nt] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(nib_base[nt] + static_cast<int64_t>(j) * WK * kTileNibBytes));
+            S.sc[nt] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(sc_base[nt] + static_cast<int64_t>(j) * WK * kTileScales));
         }
     };
 
@@ -332,6 +332,134 @@ void skinny_kernel(const LinearArgs a) {
                 else
                     sg.y[static_cast<int64_t>(m) * sg.N + n] = v;
             }
+    }
+}
+
+// ----------------------------------------------------------- skinny stream
+// Very tall weights (the LM head: thousands of 16-row tiles in one launch).
+// A grid of as many workgroups as the device holds at once, each walking the
+// tiles blockIdx.x, blockIdx.x + gridDim.x, ...  Per tile the arithmetic is
+// that of skinny_kernel<MROWS, 1, WK, P, true, WPE, false> (the same
+// super-tiles per wave, added in the same order, the same wave-ordered
+// reduction), so the results are bitwise equal to it.  x is staged in LDS
+// once per workgroup instead of once per tile, and a wave issues the load of
+// its next stage -- the next tile's, across the boundary -- as soon as a
+// stage is consumed, so the weight stream keeps running through each tile's
+// reduction.  Every wave owns KT / WK super-tiles of every tile (the
+// launcher requires KT % WK == 0), so all waves meet each tile's barrier.
+template <int MROWS, int WK, int P, int WPE>
+__global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
+void skinny_stream_kernel(const LinearArgs a, const int tiles) {
+    static_assert(MROWS <= 16 && WK > 1, "one 16-row m-tile, K split over the waves");
+    constexpr int REGS = MROWS < 4 ? MROWS : 4;
+    extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+    // wave-ordered partial sums, double-buffered by tile parity so that one
+    // barrier per tile suffices
+    __shared__ float red[2][WK - 1][REGS][64];
+    const int lane = threadIdx.x & 63;
+    const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nl = lane & 15, g = lane >> 4;
+    const int KT = a.KT;
+    const int mrows = a.M < 16 ? a.M : 16;
+    const int row_bytes = x_row_bytes(KT);
+    const int nkt = KT / WK;
+    const int stride = gridDim.x;
+    const int my_tiles = (tiles - static_cast<int>(blockIdx.x) + stride - 1) / stride;
+    const int total = my_tiles * nkt;   // stages of this wave
+
+    // the next stage to load: super-tile wk + ld_j * WK of tile ld_tile
+    int ld_tile = blockIdx.x, ld_j = 0;
+    const uint8_t *ld_nib = nullptr;
+    const uint16_t *ld_sc = nullptr;
+    auto aim = [&](int tile) {
+        const Segment &sg = a.seg[find_segment(a, tile)];
+        const int64_t T0 = static_cast<int64_t>(tile - sg.tile_begin) * KT + wk;
+        ld_nib = sg.nib + T0 * kTileNibBytes + lane * 16;
+        ld_sc = sg.scales + T0 * kTileScales + nl * 4;
+    };
+    struct WStage {
+        u32x4 nib;
+        u32x2 sc;
+    };
+    auto load_next = [&](WStage &S) {
+        S.nib = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ld_nib + static_cast<int64_t>(ld_j) * WK * kTileNibBytes));
+        S.sc = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(ld_sc + static_cast<int64_t>(ld_j) * WK * kTileScales));
+        if (++ld_j == nkt) {
+            ld_j = 0;
+            ld_tile += stride;
+            if (ld_tile < tiles) aim(ld_tile);
+        }
+    };
+
+    const int a_row = nl < mrows ? nl : mrows - 1;
+    floatx4 acc = (floatx4){0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const WStage &S, int kt) {
+#pragma unroll
+        for (int i = 0; i < kTileBlocks; ++i) {
+            const int b = kt * kTileBlocks + i;
+            const bf16x8 A = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xs + a_row * row_bytes + (b * kQK + g * 8) * 2));
+            const bf16x8 B = decode_piece(piece_of(S.nib, i));
+            const float d = scale_of(S.sc, i);
+            const floatx4 D = mfma_block(A, B);
+#pragma unroll
+            for (int r = 0; r < REGS; ++r) acc[r] = fmaf(d, D[r], acc[r]);
+        }
+    };
+
+    // 1. the first P stages, then x (zero beyond K) while they are in flight
+    aim(ld_tile);
+    WStage st[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+        if (p < total) load_next(st[p]);
+    {
+        const int chunks_per_row = KT * (kTileK / 8);
+        const int all = mrows * chunks_per_row;
+        for (int c = threadIdx.x; c < all; c += 64 * WK) {
+            const int m = c / chunks_per_row, kc = c - m * chunks_per_row;
+            u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+            if (kc * 8 < a.K) v = *reinterpret_cast<const u32x4 *>(a.x + static_cast<int64_t>(m) * a.K + kc * 8);
+            *reinterpret_cast<u32x4 *>(xs + m * row_bytes + kc * 16) = v;
+        }
+        __syncthreads();
+    }
+
+    // 2. every stage: compute, refill P stages ahead, and at a tile's last
+    //    super-tile reduce over the waves and store
+    int cj = 0, out_tile = blockIdx.x, parity = 0;
+    for (int q0 = 0; q0 < total; q0 += P) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int q = q0 + p;
+            if (q >= total) break;
+            compute(st[p], wk + cj * WK);
+            if (q + P < total) load_next(st[p]);
+            if (++cj < nkt) continue;
+            cj = 0;
+            if (wk > 0) {
+#pragma unroll
+                for (int r = 0; r < REGS; ++r) red[parity][wk - 1][r][lane] = acc[r];
+            }
+            __syncthreads();
+            if (wk == 0) {
+#pragma unroll
+                for (int w = 0; w < WK - 1; ++w)
+#pragma unroll
+                    for (int r = 0; r < REGS; ++r) acc[r] += red[parity][w][r][lane];
+                const Segment &sg = a.seg[find_segment(a, out_tile)];
+                const int n = (out_tile - sg.tile_begin) * 16 + nl;
+                if (n < sg.N) {
+#pragma unroll
+                    for (int r = 0; r < REGS; ++r) {
+                        const int m = 4 * g + r;
+                        if (m < a.M) sg.y[static_cast<int64_t>(m) * sg.N + n] = acc[r] * 16.0f;
+                    }
+                }
+            }
+            acc = (floatx4){0.f, 0.f, 0.f, 0.f};
+            out_tile += stride;
+            parity ^= 1;
+        }
     }
 }
 
@@ -806,6 +934,70 @@ int assign_tiles(LinearArgs &a, int rows_per_tile) {
     return tiles;
 }
 
+// Compute units of the current device, queried once per device (256 on
+// MI355X; also the answer when there is no device to ask).
+int device_cus() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        n = 256;
+    }
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Workgroups of a stream kernel resident per CU at this dynamic LDS size,
+// cached per device for the last size asked (1 if the runtime cannot say).
+template <typename Kernel>
+int resident_per_cu(Kernel kernel, int threads, uint32_t lds, std::atomic<uint64_t> (&cache)[64]) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 1;
+    }
+    const uint64_t v = cache[dev].load(std::memory_order_relaxed);
+    if (v != 0 && (v >> 16) == lds) return static_cast<int>(v & 0xffff);
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void *>(kernel), threads, lds) !=
+            hipSuccess || occ < 1) {
+        (void)hipGetLastError();
+        occ = 1;
+    }
+    if (occ > 0xffff) occ = 0xffff;
+    cache[dev].store((static_cast<uint64_t>(lds) << 16) | static_cast<uint64_t>(occ), std::memory_order_relaxed);
+    return occ;
+}
+
+// The stream launch: x must fit the LDS budget and KT be a multiple of WK
+// (the dispatch checks both).
+template <int MROWS, int WK, int P, int WPE>
+hipError_t run_skinny_stream(LinearArgs a, hipStream_t s) {
+    const int tiles = assign_tiles<false>(a, 1);
+    const uint32_t lds = static_cast<uint32_t>(skinny_x_bytes(a.M, a.K, MROWS));
+    auto kernel = skinny_stream_kernel<MROWS, WK, P, WPE>;
+    static std::atomic<uint64_t> lds_allowed{0};
+    const hipError_t e = allow_dynamic_lds(kernel, lds_allowed);
+    if (e != hipSuccess) return e;
+    static std::atomic<uint64_t> occ_cache[64];
+    const int64_t resident = static_cast<int64_t>(device_cus()) * resident_per_cu(kernel, 64 * WK, lds, occ_cache);
+    const int grid = static_cast<int>(tiles < resident ? tiles : resident);
+    if (t_start_event || t_stop_event) {
+        hipEvent_t start = t_start_event, stop = t_stop_event;
+        t_start_event = t_stop_event = nullptr;
+        hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(64 * WK), lds, s, start, stop, 0, a, tiles);
+    } else {
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * WK), lds, s, a, tiles);
+    }
+    return hipGetLastError();
+}
+
 template <int MROWS, int NT, int WK, int P, int WPE = 0, bool GLU = false>
 hipError_t run_skinny(LinearArgs a, hipStream_t s) {
     const int tiles = assign_tiles<GLU>(a, NT);
@@ -856,6 +1048,14 @@ void arm_launch_events(hipEvent_t start, hipEvent_t stop) {
     t_stop_event = stop;
 }
 
+bool take_launch_events(hipEvent_t &start, hipEvent_t &stop) {
+    if (!t_start_event && !t_stop_event) return false;
+    start = t_start_event;
+    stop = t_stop_event;
+    t_start_event = t_stop_event = nullptr;
+    return true;
+}
+
 // The dispatch table.  Decode sizes (M <= 64) pick by M and K: skinny
 // kernels split K over the waves of a workgroup with a short prefetch, so
 // that many waves stay resident (the launches are latency-bound); long rows
@@ -874,7 +1074,7 @@ void arm_launch_events(hipEvent_t start, hipEvent_t stop) {
 // results of an output in the same order, so the choice never changes a
 // result.
 namespace {
-enum class Cfg { M1, M1Long, M2, M2Long, M4, M4Long, M16, M16Long, M32, M64, Gemm64, Gemm128, Gemm128W };
+enum class Cfg { M1, M1Stream, M1Long, M2, M2Long, M4, M4Long, M16, M16Long, M32, M64, Gemm64, Gemm128, Gemm128W };
 
 // Configuration by M and K alone: the decode sizes, and the gated launch's
 // GEMM split at 2048 rows.
@@ -889,25 +1089,6 @@ Cfg pick_mk(int64_t M, int64_t K) {
     return M < 2048 ? Cfg::Gemm64 : Cfg::Gemm128;
 }
 
-// Compute units of the current device, queried once per device (256 on
-// MI355X; also the answer when there is no device to ask).
-int device_cus() {
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
-        (void)hipGetLastError();
-        return 256;
-    }
-    int n = cached[dev].load(std::memory_order_relaxed);
-    if (n > 0) return n;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
-        (void)hipGetLastError();
-        n = 256;
-    }
-    cached[dev].store(n, std::memory_order_relaxed);
-    return n;
-}
-
 // Work tiles of a BM x BN GEMM tiling over all segments of a launch.
 int64_t gemm_tiles(const LinearArgs &a, int bm, int bn) {
     const int rows_per_tile = bn / kTileRows;
@@ -916,8 +1097,20 @@ int64_t gemm_tiles(const LinearArgs &a, int bm, int bn) {
     return ntiles * ((a.M + bm - 1) / bm);
 }
 
+// One row of x and at least 8 row tiles per CU (the LM head: 8192 tiles on
+// 256 CUs): the stream kernel, when x fits in LDS and K splits evenly over
+// its 8 waves.
+bool stream_m1(const LinearArgs &a) {
+    int64_t rts = 0;
+    for (int i = 0; i < a.nseg; ++i) rts += a.seg[i].RT;
+    return a.KT % 8 == 0 && skinny_x_bytes(a.M, a.K, 1) <= xlds_budget(1) && rts >= 8 * static_cast<int64_t>(device_cus());
+}
+
 Cfg pick(const LinearArgs &a) {
-    if (a.M <= 64) return pick_mk(a.M, a.K);
+    if (a.M <= 64) {
+        const Cfg c = pick_mk(a.M, a.K);
+        return c == Cfg::M1 && stream_m1(a) ? Cfg::M1Stream : c;
+    }
     const int64_t cus = device_cus();
     auto cost = [&](int bm, int bn, int64_t unit) { return (gemm_tiles(a, bm, bn) + cus - 1) / cus * unit; };
     const int64_t c64 = cost(64, 128, 30), c128 = cost(128, 128, 50), c128w = cost(128, 192, 85);
@@ -935,6 +1128,7 @@ const char *linear_config_name(const LinearArgs &a) {
     const int64_t M = a.M, K = a.K;
     switch (pick(a)) {
         case Cfg::M1: return skinny_name(M, K, 1, "skinny_kernel<1, 1, 8, 3, true, 6, false>", "skinny_kernel<1, 1, 8, 3, false, 6, false>");
+        case Cfg::M1Stream: return "skinny_stream_kernel<1, 8, 3, 6>";
         case Cfg::M1Long: return skinny_name(M, K, 1, "skinny_kernel<1, 1, 16, 2, true, 0, false>", "skinny_kernel<1, 1, 16, 2, false, 0, false>");
         case Cfg::M2: return skinny_name(M, K, 2, "skinny_kernel<2, 1, 4, 2, true, 6, false>", "skinny_kernel<2, 1, 4, 2, false, 6, false>");
         case Cfg::M2Long: return skinny_name(M, K, 2, "skinny_kernel<2, 1, 16, 2, true, 0, false>", "skinny_kernel<2, 1, 16, 2, false, 0, false>");
@@ -953,6 +1147,7 @@ const char *linear_config_name(const LinearArgs &a) {
 hipError_t launch_linear(LinearArgs a, hipStream_t s) {
     switch (pick(a)) {
         case Cfg::M1: return run_skinny<1, 1, 8, 3, 6>(a, s);
+        case Cfg::M1Stream: return run_skinny_stream<1, 8, 3, 6>(a, s);
         case Cfg::M1Long: return run_skinny<1, 1, 16, 2, 0>(a, s);
         case Cfg::M2: return run_skinny<2, 1, 4, 2, 6>(a, s);
         case Cfg::M2Long: return run_skinny<2, 1, 16, 2, 0>(a, s);
