@@ -143,7 +143,10 @@ typedef struct {
  * Several weight matrices sharing x and K in one launch (fused QKV: three
  * segments 4096/1024/1024; fused gate/up: two of 9216).  `segs` is host
  * memory with nseg entries, 1 <= nseg <= 8; each segment is validated like a
- * q4_0_linear call.  Equal, segment by segment, to separate q4_0_linear calls.
+ * q4_0_linear call.  Each segment's result meets the q4_0_linear bound, and
+ * equals a separate q4_0_linear call bit for bit whenever both run the same
+ * kernel family (see q4_0_linear_kernel: the choice can depend on the total
+ * tile count at M = 1 for very tall weights and at 17 rows and more).
  */
 q4_status q4_0_linear_multi(const void *x_bf16, int64_t M, int64_t K, const q4_0_segment *segs,
                             int nseg, void *stream);
@@ -178,13 +181,17 @@ const char *q4_0_linear_swiglu_kernel(int64_t M, int64_t K);
 /*
  * Name of the kernel instantiation q4_0_linear_multi runs for M, K and the
  * segments' row counts N[0 .. nseg-1] (host array; q4_0_linear is nseg = 1).
- * Up to 64 rows the configuration depends on M and K only; above, the GEMM
- * tile shape also depends on how many work tiles the segments make and on the
- * current device's compute-unit count (256 is assumed when no device answers).
- * The tile shapes add the block results of an output in the same order, so a
- * fused launch and separate launches of its segments give bitwise equal
- * results whichever shapes they run.  Static string; "" for an invalid
- * argument.  For reports that match timings to kernel names.
+ * The choice depends on M and K, and also on how many work tiles the segments
+ * make against the current device's compute-unit count (256 is assumed when
+ * no device answers): at M = 1 for very tall weights (a fixed-grid walk of
+ * the same per-tile arithmetic), at 17-64 rows (the K-split decode kernel for
+ * short weights, the GEMM for tall ones) and above 64 rows (the GEMM tile
+ * shape).  A fused launch and separate launches of its segments give bitwise
+ * equal results when they run the same kernel family (the tile shapes of the
+ * GEMM add an output's block results in the same order, and so do the decode
+ * kernels for one M); across families they agree within the stated bound.
+ * Static string; "" for an invalid argument.  For reports that match timings
+ * to kernel names.
  */
 const char *q4_0_linear_kernel(int64_t M, int64_t K, const int64_t *N, int nseg);
 

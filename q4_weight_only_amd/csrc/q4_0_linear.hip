@@ -13,13 +13,16 @@
 // dequantization split so that no weight is ever rounded.
 //
 // Kernels.
-//   skinny_kernel  (M <= 16, decode-sized batches): a wave owns all M rows,
+//   skinny_kernel  (M <= 16, decode-sized batches; also 17-64 rows when the
+//                  weights are short): a wave owns all M rows,
 //                  NT 16-row weight tiles and every WK-th super-tile along K;
 //                  weights go straight from HBM into MFMA B registers (each
 //                  lane's 16-byte load is exactly its B slice for 4 blocks),
 //                  x comes from LDS (staged once) or global memory, and the WK
 //                  waves of a workgroup are summed through LDS in a fixed order.
-//   gemm_kernel    (17 <= M <= 64): a workgroup tile of BM x BN outputs; the x
+//   skinny_stream_kernel (M = 1, very tall weights): the same per tile, with a
+//                  fixed grid walking the tiles.
+//   gemm_kernel    (17 <= M <= 64, tall weights): a workgroup tile of BM x BN outputs; the x
 //                  tile of each 128-k step is staged in LDS (double-buffered,
 //                  XOR-swizzled 16-byte chunks) and shared by the WN waves;
 //                  weights again go HBM -> registers.
@@ -124,7 +127,7 @@ __device__ __forceinline__ int x_row_bytes(int KT) { return KT * kTileK * 2 + 16
 
 template <int MROWS, int NT, int WK, int P, bool XLDS, int WPE, bool GLU>
 struct SkinnyCfg {
-    static constexpr int MT = MROWS > 16 ? 2 : 1;        // 16-row m-tiles
+    static constexpr int MT = (MROWS + 15) / 16;         // 16-row m-tiles
     static constexpr int REGS = MROWS < 4 ? MROWS : 4;   // live accumulator rows per lane
     static constexpr int kWaves = GLU ? 2 * WK : WK;     // waves per workgroup
     static constexpr int kThreads = 64 * kWaves;
@@ -1002,7 +1005,7 @@ template <int MROWS, int NT, int WK, int P, int WPE = 0, bool GLU = false>
 hipError_t run_skinny(LinearArgs a, hipStream_t s) {
     const int tiles = assign_tiles<GLU>(a, NT);
     constexpr int kThreads = 64 * WK * (GLU ? 2 : 1);
-    static_assert(MROWS <= 16, "x staging covers one 16-row m-tile");
+    static_assert(MROWS <= 64, "at most four 16-row m-tiles per wave");
     const uint64_t lds = skinny_x_bytes(a.M, a.K, MROWS);
     if (lds <= xlds_budget(MROWS)) {
         auto kernel = skinny_kernel<MROWS, NT, WK, P, true, WPE, GLU>;
@@ -1074,7 +1077,8 @@ bool take_launch_events(hipEvent_t &start, hipEvent_t &stop) {
 // results of an output in the same order, so the choice never changes a
 // result.
 namespace {
-enum class Cfg { M1, M1Stream, M1Long, M2, M2Long, M4, M4Long, M16, M16Long, M32, M64, Gemm64, Gemm128, Gemm128W };
+enum class Cfg { M1, M1Stream, M1Long, M2, M2Long, M4, M4Long, M16, M16Long, M32, M32Split, M32Split2, M64, M64Split,
+                 Gemm64, Gemm128, Gemm128W };
 
 // Configuration by M and K alone: the decode sizes, and the gated launch's
 // GEMM split at 2048 rows.
@@ -1106,9 +1110,27 @@ bool stream_m1(const LinearArgs &a) {
     return a.KT % 8 == 0 && skinny_x_bytes(a.M, a.K, 1) <= xlds_budget(1) && rts >= 8 * static_cast<int64_t>(device_cus());
 }
 
+// 17-64 rows: the GEMM's 128-column tiles number under half the CUs (every
+// N of a few thousand rows: 24 tiles for N = 3072) leave most of the chip
+// idle, and the decode kernel's K split over 8 waves runs 2-3x faster there
+// (measured at M = 32 and 64); tall weights (gate/up, the LM head) keep the
+// GEMM.  32 rows: two row tiles per wave once the row tiles outnumber the CUs.
+Cfg pick_17_64(const LinearArgs &a, Cfg gemm) {
+    int64_t rts = 0, tiles = 0;
+    for (int i = 0; i < a.nseg; ++i) {
+        rts += a.seg[i].RT;
+        tiles += (a.seg[i].RT + 7) / 8;
+    }
+    const int64_t cus = device_cus();
+    if (2 * tiles >= cus) return gemm;
+    if (gemm == Cfg::M64) return Cfg::M64Split;
+    return rts >= cus ? Cfg::M32Split2 : Cfg::M32Split;
+}
+
 Cfg pick(const LinearArgs &a) {
     if (a.M <= 64) {
         const Cfg c = pick_mk(a.M, a.K);
+        if (c == Cfg::M32 || c == Cfg::M64) return pick_17_64(a, c);
         return c == Cfg::M1 && stream_m1(a) ? Cfg::M1Stream : c;
     }
     const int64_t cus = device_cus();
@@ -1137,7 +1159,10 @@ const char *linear_config_name(const LinearArgs &a) {
         case Cfg::M16: return skinny_name(M, K, 16, "skinny_kernel<16, 1, 4, 2, true, 0, false>", "skinny_kernel<16, 1, 4, 2, false, 0, false>");
         case Cfg::M16Long: return skinny_name(M, K, 16, "skinny_kernel<16, 1, 16, 2, true, 0, false>", "skinny_kernel<16, 1, 16, 2, false, 0, false>");
         case Cfg::M32: return "gemm_kernel<2, 1, 1, 8, 0>";
+        case Cfg::M32Split: return skinny_name(M, K, 32, "skinny_kernel<32, 1, 8, 2, true, 0, false>", "skinny_kernel<32, 1, 8, 2, false, 0, false>");
+        case Cfg::M32Split2: return skinny_name(M, K, 32, "skinny_kernel<32, 2, 8, 2, true, 0, false>", "skinny_kernel<32, 2, 8, 2, false, 0, false>");
         case Cfg::M64: return "gemm_kernel<4, 1, 1, 8, 0>";
+        case Cfg::M64Split: return skinny_name(M, K, 64, "skinny_kernel<64, 1, 8, 2, true, 0, false>", "skinny_kernel<64, 1, 8, 2, false, 0, false>");
         case Cfg::Gemm64: return "gemm3_kernel<4, 1, 1, 8, 4, 8, false>";
         case Cfg::Gemm128W: return "gemm3_kernel<8, 1, 1, 12, 0, 8, false>";
         default: return "gemm3_kernel<8, 1, 1, 8, 4, 8, false>";
@@ -1156,7 +1181,10 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
         case Cfg::M16: return run_skinny<16, 1, 4, 2, 0>(a, s);
         case Cfg::M16Long: return run_skinny<16, 1, 16, 2, 0>(a, s);
         case Cfg::M32: return run_gemm<2, 1, 1, 8, 0>(a, s);
+        case Cfg::M32Split: return run_skinny<32, 1, 8, 2, 0>(a, s);
+        case Cfg::M32Split2: return run_skinny<32, 2, 8, 2, 0>(a, s);
         case Cfg::M64: return run_gemm<4, 1, 1, 8, 0>(a, s);
+        case Cfg::M64Split: return run_skinny<64, 1, 8, 2, 0>(a, s);
         case Cfg::Gemm64: return run_gemm3<4, 1, 1, 8, 4, 8>(a, s);
         case Cfg::Gemm128W: return run_gemm3<8, 1, 1, 12, 0, 8>(a, s);
         default: return run_gemm3<8, 1, 1, 8, 4, 8>(a, s);

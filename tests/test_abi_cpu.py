@@ -142,11 +142,19 @@ def test_linear_kernel_names(L):
     assert kn(1, 64, arr(*([16] * 9)), 9) == b""        # too many segments
     assert kn(1, 64, None, 1) == b""
     assert kn(1, 3072, arr(4096, 1024, 1024), 3).startswith(b"skinny_kernel<1, ")
-    assert kn(20, 3072, arr(3072), 1) == b"gemm_kernel<2, 1, 1, 8, 0>"
-    assert kn(40, 3072, arr(3072), 1) == b"gemm_kernel<4, 1, 1, 8, 0>"
     import torch
     if torch.cuda.is_available() and torch.cuda.get_device_properties(0).multi_processor_count != 256:
         return                                          # the tile counts below assume 256 CUs
+    # 17-64 rows: the K-split decode kernel under 128 GEMM tiles, the GEMM from there
+    assert kn(20, 3072, arr(3072), 1) == b"skinny_kernel<32, 1, 8, 2, false, 0, false>"
+    assert kn(20, 3072, arr(4096, 1024, 1024), 3) == b"skinny_kernel<32, 2, 8, 2, false, 0, false>"
+    assert kn(20, 256, arr(3072), 1) == b"skinny_kernel<32, 1, 8, 2, true, 0, false>"
+    assert kn(40, 3072, arr(3072), 1) == b"skinny_kernel<64, 1, 8, 2, false, 0, false>"
+    assert kn(20, 3072, arr(16384), 1) == b"gemm_kernel<2, 1, 1, 8, 0>"
+    assert kn(40, 3072, arr(131072), 1) == b"gemm_kernel<4, 1, 1, 8, 0>"
+    # one row: very tall weights take the stream kernel
+    assert kn(1, 3072, arr(131072), 1) == b"skinny_stream_kernel<1, 8, 3, 6>"
+    assert kn(1, 3072, arr(9216, 9216), 2) == b"skinny_kernel<1, 1, 8, 3, true, 6, false>"
     assert kn(2048, 4096, arr(3072), 1) == b"gemm3_kernel<8, 1, 1, 12, 0, 8, false>"
     assert kn(2048, 3072, arr(3072, 3072, 3072), 3) == b"gemm3_kernel<8, 1, 1, 8, 4, 8, false>"
     assert kn(300, 3072, arr(3072), 1) == b"gemm3_kernel<4, 1, 1, 8, 4, 8, false>"

@@ -1,8 +1,8 @@
 """Parity of the device linear with the oracle on sizes the oracle finishes in
 seconds: every output element within 1e-3 * sum|x w| + 1e-6, across the
-kernel variants (M = 1, 2, 3-4, 5-16, 17-32, 33-64, 65-2047, >= 2048), several
-tiles in N and K,
-ragged edges, structured weights, fused segments and determinism."""
+kernel variants (M = 1, 2, 3-4, 5-16, 17-32, 33-64 on short and on tall
+weights, 65-2047, >= 2048), several tiles in N and K, ragged edges,
+structured weights, fused segments and determinism."""
 
 import numpy as np
 import pytest
@@ -101,6 +101,20 @@ def test_reads_no_activation_beyond_k(m):
     say("nan tail", m)
     y = q4.linear(xv, pw).cpu().numpy()
     assert_within_bound(y, O.linear(x, blocks, n, k), O.error_bound(x, blocks, n, k), "nan tail")
+
+
+@pytest.mark.parametrize("m", [17, 32, 40, 64])
+def test_17_to_64_rows_on_tall_weights(m):
+    """17-64 rows take the GEMM only on weights of at least half a tile per CU
+    (129 tiles of 128 rows here); short weights, as in the grid above, take
+    the K-split decode kernel.  Every output element against the oracle."""
+    n, k = 16400, 256
+    w = inputs.weights_f32((n, k), seed=22, tags=(n, k))
+    x = inputs.activations_bf16((m, k), seed=22, tags=(m, k))
+    name = q4.linear_kernel(m, k, n)
+    if torch.cuda.get_device_properties(DEV).multi_processor_count <= 256:
+        assert name.startswith("gemm_kernel<"), name
+    _run_and_check(w, x, f"M={m} N={n} K={k} {name}")
 
 
 @pytest.mark.parametrize("m", [1, 2, 3, 17, 32, 40, 300])

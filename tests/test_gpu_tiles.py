@@ -40,11 +40,20 @@ def test_tile_shapes_agree_bitwise():
     for i in (1, 2):
         assert np.array_equal(_bits(q4.linear(x, pws[i])), _bits(y_fused[i]))
 
-    # fewer rows of x: other tile shapes, and the 17-64-row GEMM
-    for rows in (1500, 300, 64, 40):
+    # fewer rows of x: other tile shapes
+    for rows in (1500, 300):
         say("tiles rows", rows, q4.linear_kernel(rows, k, ns[0]))
         y = q4.linear(x[:rows], pws[0])
         assert np.array_equal(_bits(y), _bits(y_single[:rows])), f"M={rows}"
+    # and the 17-64-row GEMM, on weights tall enough to take it
+    tall = 8 * 16 * 129
+    wt = inputs.weights_f32((tall, k), seed=81, tags=(tall,))
+    pt, _ = device_weight_from_f32(wt)
+    yt = q4.linear(x, pt)
+    for rows in (64, 40):
+        assert q4.linear_kernel(rows, k, tall).startswith("gemm_kernel<")
+        say("tiles rows", rows, q4.linear_kernel(rows, k, tall))
+        assert np.array_equal(_bits(q4.linear(x[:rows], pt)), _bits(yt[:rows])), f"M={rows}"
 
     # the single launch against the oracle on sampled rows of W
     cols = sample_rows(ns[0], 48, 81)
