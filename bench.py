@@ -12,6 +12,7 @@ graph and replayed; K replays are timed with HIP events on the replay stream.
 Printed (one JSON line):
   value       eff. HBM GB/s of the whole step: algorithmic bytes per step
               (packed weights + x + y) * K / elapsed
+  decode_m2   the same step at M=2 (the batched CFG pair): us/step and GB/s
   roofline    the dominant kernel (the M=1 decode kernel) against 8 TB/s:
               algorithmic bytes of its launches / their summed kernel-own
               durations, taken with events armed on each launch of the timed
@@ -433,7 +434,7 @@ def main():
     _, decode = inputs.workload(2)
     specs = [s for s, _ in decode][: 4 * args.layers]
     t0 = time.time()
-    prepared = build_device_specs(specs, (1,), dev)
+    prepared = build_device_specs(specs, (1, 2), dev)
     log(f"decode workload ready: {len(specs)} launches, {sum(s.weight_bytes() for s in specs) / 1e9:.3f} GB "
         f"of Q4_0 weights ({time.time() - t0:.1f} s)")
     runner = Runner(prepared, 1, dev)
@@ -500,6 +501,22 @@ def main():
         },
         "roofline": roofline,
     }
+
+    # ---- the same step at M=2 (the batched CFG pair of the decode workload)
+    runner2 = Runner(prepared, 2, dev)
+    el2, graph2 = time_graph(runner2, args.steps, args.warmup, dev)
+    del graph2
+    gbs2 = runner2.bytes_per_step() * args.steps / el2 / 1e9
+    out["decode_m2"] = {
+        "workload": "the decode step at M=2 (batched CFG pair), same weights and launches",
+        "us_per_step": round(el2 / args.steps * 1e6, 1),
+        "value": round(gbs2, 1),
+        "unit": "GB/s",
+        "frac_of_8TBs": round(gbs2 / HBM_PEAK_GBS, 4),
+        "kernels": sorted({q4.linear_kernel(2, spec.K, spec.Ns) for spec, *_ in runner2.items}),
+    }
+    log(f"decode M=2: {out['decode_m2']['us_per_step']} us/step, {gbs2:.1f} GB/s")
+    del runner2
 
     # ---- prefill (M=2048 through the four decoder shapes, layer-0 weights)
     if not args.no_prefill:
