@@ -488,9 +488,14 @@ __device__ __forceinline__ int a_tile_offset(int m, int c) { return (m * 16 + (c
 constexpr int kBufferRsrcWord3 = 0x00020000;
 constexpr int kOutOfRange = 0x40000000;   // a byte offset beyond every x resource (at most 2^29 bytes)
 
-template <int MT, int NT, int WM, int WN, int WPE>
+// PB weight stages per wave: the loads for step kt + PB - 1 are issued while
+// step kt computes (the x tile is double-buffered in LDS either way).  Each
+// weight tile is read by one workgroup per 64 rows of x, so the weight loads
+// are nontemporal.
+template <int MT, int NT, int WM, int WN, int WPE, int PB>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
 void gemm_kernel(const LinearArgs a) {
+    static_assert(PB >= 2, "at least one step of weights in flight");
     using C = GemmCfg<MT, NT, WM, WN>;
     constexpr int BM = C::BM, NPT = C::kAPerThread;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * 256];
@@ -549,8 +554,8 @@ void gemm_kernel(const LinearArgs a) {
     auto load_b = [&](BStage &S, int kt) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            S.nib[nt] = *reinterpret_cast<const u32x4 *>(nib_base[nt] + static_cast<int64_t>(kt) * kTileNibBytes);
-            S.sc[nt] = *reinterpret_cast<const u32x2 *>(sc_base[nt] + static_cast<int64_t>(kt) * kTileScales);
+            S.nib[nt] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(nib_base[nt] + static_cast<int64_t>(kt) * kTileNibBytes));
+            S.sc[nt] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(sc_base[nt] + static_cast<int64_t>(kt) * kTileScales));
         }
     };
 
@@ -592,35 +597,34 @@ void gemm_kernel(const LinearArgs a) {
         }
     };
 
-    BStage b0, b1;
+    // step kt: x from LDS buffer kt % 2, weights from stage kt % PB; the loop
+    // is unrolled so both indices are static.  Loads past the last step are
+    // clamped to it (their stages are never used).
+    constexpr int U = PB % 2 == 0 ? PB : 2 * PB;
+    BStage W[PB];
+#pragma unroll
+    for (int p = 0; p < PB - 1; ++p) load_b(W[p], p < KT ? p : KT - 1);
     load_a(0);
-    load_b(b0, 0);
     store_a(0);
     __syncthreads();
-    int kt = 0;
-    for (;;) {
-        // even step: compute kt from buffer 0 / b0, prefetch kt+1 into buffer 1 / b1
-        const bool more0 = kt + 1 < KT;
-        if (more0) {
-            load_a(kt + 1);
-            load_b(b1, kt + 1);
+    for (int kt0 = 0;; kt0 += U) {
+        bool done = false;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kt = kt0 + u;
+            const int kp = kt + PB - 1;
+            load_b(W[(u + PB - 1) % PB], kp < KT ? kp : KT - 1);
+            const bool more = kt + 1 < KT;
+            if (more) load_a(kt + 1);
+            compute(u % 2, W[u % PB]);
+            if (!more) {
+                done = true;
+                break;
+            }
+            store_a((u + 1) % 2);
+            __syncthreads();
         }
-        compute(0, b0);
-        if (!more0) break;
-        store_a(1);
-        __syncthreads();
-        ++kt;
-        // odd step
-        const bool more1 = kt + 1 < KT;
-        if (more1) {
-            load_a(kt + 1);
-            load_b(b0, kt + 1);
-        }
-        compute(1, b1);
-        if (!more1) break;
-        store_a(0);
-        __syncthreads();
-        ++kt;
+        if (done) break;
     }
 
 #pragma unroll
@@ -1017,12 +1021,12 @@ hipError_t run_skinny(LinearArgs a, hipStream_t s) {
     return launch_kernel(skinny_kernel<MROWS, NT, WK, P, false, WPE, GLU>, dim3(tiles), dim3(kThreads), 0, s, a);
 }
 
-template <int MT, int NT, int WM, int WN, int WPE = 0>
+template <int MT, int NT, int WM, int WN, int WPE = 0, int PB = 2>
 hipError_t run_gemm(LinearArgs a, hipStream_t s) {
     using C = GemmCfg<MT, NT, WM, WN>;
     const int tiles = assign_tiles<false>(a, NT * WN);
     const int mtiles = (a.M + C::BM - 1) / C::BM;
-    return launch_kernel(gemm_kernel<MT, NT, WM, WN, WPE>, dim3(tiles, mtiles), dim3(C::kThreads), 0, s, a);
+    return launch_kernel(gemm_kernel<MT, NT, WM, WN, WPE, PB>, dim3(tiles, mtiles), dim3(C::kThreads), 0, s, a);
 }
 
 template <int MT, int NT, int WM, int WN, int WPE = 0, int GM = 8, bool GLU = false>
@@ -1158,10 +1162,10 @@ const char *linear_config_name(const LinearArgs &a) {
         case Cfg::M4Long: return skinny_name(M, K, 4, "skinny_kernel<4, 1, 16, 2, true, 0, false>", "skinny_kernel<4, 1, 16, 2, false, 0, false>");
         case Cfg::M16: return skinny_name(M, K, 16, "skinny_kernel<16, 1, 4, 2, true, 0, false>", "skinny_kernel<16, 1, 4, 2, false, 0, false>");
         case Cfg::M16Long: return skinny_name(M, K, 16, "skinny_kernel<16, 1, 16, 2, true, 0, false>", "skinny_kernel<16, 1, 16, 2, false, 0, false>");
-        case Cfg::M32: return "gemm_kernel<2, 1, 1, 8, 0>";
+        case Cfg::M32: return "gemm_kernel<2, 1, 1, 8, 0, 2>";
         case Cfg::M32Split: return skinny_name(M, K, 32, "skinny_kernel<32, 1, 8, 2, true, 0, false>", "skinny_kernel<32, 1, 8, 2, false, 0, false>");
         case Cfg::M32Split2: return skinny_name(M, K, 32, "skinny_kernel<32, 2, 8, 2, true, 0, false>", "skinny_kernel<32, 2, 8, 2, false, 0, false>");
-        case Cfg::M64: return "gemm_kernel<4, 1, 1, 8, 0>";
+        case Cfg::M64: return "gemm_kernel<4, 1, 1, 8, 0, 3>";
         case Cfg::M64Split: return skinny_name(M, K, 64, "skinny_kernel<64, 1, 8, 2, true, 0, false>", "skinny_kernel<64, 1, 8, 2, false, 0, false>");
         case Cfg::Gemm64: return "gemm3_kernel<4, 1, 1, 8, 4, 8, false>";
         case Cfg::Gemm128W: return "gemm3_kernel<8, 1, 1, 12, 0, 8, false>";
@@ -1180,10 +1184,10 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
         case Cfg::M4Long: return run_skinny<4, 1, 16, 2, 0>(a, s);
         case Cfg::M16: return run_skinny<16, 1, 4, 2, 0>(a, s);
         case Cfg::M16Long: return run_skinny<16, 1, 16, 2, 0>(a, s);
-        case Cfg::M32: return run_gemm<2, 1, 1, 8, 0>(a, s);
+        case Cfg::M32: return run_gemm<2, 1, 1, 8, 0, 2>(a, s);
         case Cfg::M32Split: return run_skinny<32, 1, 8, 2, 0>(a, s);
         case Cfg::M32Split2: return run_skinny<32, 2, 8, 2, 0>(a, s);
-        case Cfg::M64: return run_gemm<4, 1, 1, 8, 0>(a, s);
+        case Cfg::M64: return run_gemm<4, 1, 1, 8, 0, 3>(a, s);
         case Cfg::M64Split: return run_skinny<64, 1, 8, 2, 0>(a, s);
         case Cfg::Gemm64: return run_gemm3<4, 1, 1, 8, 4, 8>(a, s);
         case Cfg::Gemm128W: return run_gemm3<8, 1, 1, 12, 0, 8>(a, s);

@@ -150,8 +150,8 @@ def test_linear_kernel_names(L):
     assert kn(20, 3072, arr(4096, 1024, 1024), 3) == b"skinny_kernel<32, 2, 8, 2, false, 0, false>"
     assert kn(20, 256, arr(3072), 1) == b"skinny_kernel<32, 1, 8, 2, true, 0, false>"
     assert kn(40, 3072, arr(3072), 1) == b"skinny_kernel<64, 1, 8, 2, false, 0, false>"
-    assert kn(20, 3072, arr(16384), 1) == b"gemm_kernel<2, 1, 1, 8, 0>"
-    assert kn(40, 3072, arr(131072), 1) == b"gemm_kernel<4, 1, 1, 8, 0>"
+    assert kn(20, 3072, arr(16384), 1) == b"gemm_kernel<2, 1, 1, 8, 0, 2>"
+    assert kn(40, 3072, arr(131072), 1) == b"gemm_kernel<4, 1, 1, 8, 0, 3>"
     # one row: very tall weights take the stream kernel
     assert kn(1, 3072, arr(131072), 1) == b"skinny_stream_kernel<1, 8, 3, 6>"
     assert kn(1, 3072, arr(9216, 9216), 2) == b"skinny_kernel<1, 1, 8, 3, true, 6, false>"
