@@ -1063,10 +1063,12 @@ bool take_launch_events(hipEvent_t &start, hipEvent_t &stop) {
     return true;
 }
 
-// The dispatch table.  Decode sizes (M <= 64) pick by M and K: skinny
+// The dispatch table.  Decode sizes (M <= 16) pick by M and K: skinny
 // kernels split K over the waves of a workgroup with a short prefetch, so
 // that many waves stay resident (the launches are latency-bound); long rows
-// (K > 3072) split K wider.  Above 64 rows three GEMM tile shapes compete on
+// (K > 3072) split K wider; one row over very tall weights walks the tiles
+// with a fixed grid.  17-64 rows choose between the K-split kernel and the
+// GEMM by tile count (pick_17_64).  Above 64 rows three GEMM tile shapes compete on
 // how evenly their work tiles spread over the device's compute units:
 //   gemm3 64 x 128   (two workgroups per CU),
 //   gemm3 128 x 128  (two workgroups per CU),
