@@ -26,6 +26,13 @@ def test_graph_replays_match_eager():
     x1 = to_dev_x(inputs.activations_bf16((1, k), seed=71, tags=(1,)))
     x2 = to_dev_x(inputs.activations_bf16((300, k), seed=71, tags=(300,)))
     ids = torch.tensor([5, 0, 255, 17, 17, -3], dtype=torch.int32, device=DEV)
+    # a tall one-row launch: the stream kernel (fixed grid walking 2560 tiles)
+    tall, kt = 40960, 1024
+    ptall, _ = device_weight_from_f32(inputs.weights_f32((tall, kt), seed=71, tags=(9,)))
+    xt = to_dev_x(inputs.activations_bf16((1, kt), seed=71, tags=(9,)))
+    yt = torch.empty((1, tall), device=DEV)
+    assert q4.linear_kernel(1, kt, tall).startswith("skinny_stream_kernel") or \
+        torch.cuda.get_device_properties(DEV).multi_processor_count > 256
 
     ys1 = [torch.empty((1, n), device=DEV) for n in ns]
     y2 = torch.empty((300, ns[0]), device=DEV)
@@ -37,11 +44,12 @@ def test_graph_replays_match_eager():
         q4.linear(x2, pws[0], y2)
         q4.linear_swiglu(x2, gate, up, h)
         q4.embed(pws[0], ids, e)
+        q4.linear(xt, ptall, yt)
 
     say("graph eager")
     work()
     torch.cuda.synchronize()
-    eager = [t.clone() for t in (*ys1, y2, h, e)]
+    eager = [t.clone() for t in (*ys1, y2, h, e, yt)]
 
     stream = torch.cuda.Stream(DEV)
     stream.wait_stream(torch.cuda.current_stream(DEV))
@@ -49,7 +57,7 @@ def test_graph_replays_match_eager():
     with torch.cuda.graph(graph, stream=stream):
         work()
     torch.cuda.synchronize()
-    outs = (*ys1, y2, h, e)
+    outs = (*ys1, y2, h, e, yt)
     for rep in range(4):
         for t in outs:
             t.fill_(float("nan"))          # eager work between replays
