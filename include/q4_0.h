@@ -4,8 +4,8 @@
  *
  * The operation.  The quantized Voxtral checkpoints store their linear
  * weights as GGUF Q4_0 ("Voxtral Mini 4B Realtime (Rust) -- Shannon-Prime
- * Fork", section "RTF Benchmark Results": "Voxtral Mini 4B Q4_0 GGUF"; hakusoku
- * summary "Voxtral Mini 4B Realtime 概要", section "推論パス": "GGUF Q4_0"), and
+ * Fork", section "RTF Benchmark Results"; hakusoku summary "Voxtral Mini 4B
+ * Realtime 概要", section "推論パス"), and
  * the Rust engine multiplies them with a shader that fuses dequantization into
  * the matmul (hakusoku summary, section "線形演算・埋め込み").  The format:
  * W is [N, K] (N outputs, K inputs, K a multiple of 32); each run of 32

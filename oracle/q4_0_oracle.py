@@ -8,9 +8,9 @@ What the oracle computes, and where each step comes from:
 
 * The weight format is GGUF Q4_0, the format named for the quantized Voxtral
   checkpoints ("Voxtral Mini 4B Realtime (Rust) -- Shannon-Prime Fork",
-  section "RTF Benchmark Results": model "Voxtral Mini 4B Q4_0 GGUF"; and the
-  hakusoku summary page "Voxtral Mini 4B Realtime 概要", section "推論パス",
-  "GGUF Q4_0").  A block holds 32 consecutive weights of one output row: an
+  section "RTF Benchmark Results", which lists the Q4_0 GGUF model; and the
+  hakusoku summary page "Voxtral Mini 4B Realtime 概要", section "推論パス").
+  A block holds 32 consecutive weights of one output row: an
   fp16 scale d followed by 16 bytes of 4-bit codes q, and a weight decodes as
   w = (q - 8) * d.  Byte j of the 16 holds element j in its low nibble and
   element j + 16 in its high nibble.  18 bytes per 32 weights is what the
@@ -18,9 +18,9 @@ What the oracle computes, and where each step comes from:
   embedding is 216 MB there (131072 * 3072 / 32 * 18 B = 216 MiB).
 * The layer is y = x W^T with W stored [N, K] (output rows, input columns)
   and x given as bf16, y returned in fp64 here (fp32 on the device).  The
-  pages fuse dequantization into the matmul ("線形演算": a custom WGSL shader
-  fusing dequant + matmul); fusion changes no arithmetic, so the oracle is the
-  unfused definition: dequantize, then multiply.
+  pages' engine folds the dequantization into a WGSL matmul shader (hakusoku,
+  section "線形演算・埋め込み"); fusion changes no arithmetic, so the oracle is
+  the unfused definition: dequantize, then multiply.
 * Quantizer (host, off the timed path; the pages' counterpart is the offline
   script scripts/quantize_tts_gguf.py in "Model Preparation"): per block the
   signed element of largest magnitude (lowest index on ties) is amax,
