@@ -350,10 +350,18 @@ def time_lm_head(spec, pw, ms, reps, dev):
 
 
 def kernel_source_digest():
+    """Hash of the linear kernels' source with comments and whitespace
+    removed, so the stored counter record stays valid across comment edits
+    and goes stale on any change to the code."""
+    import re
+
     h = hashlib.sha256()
     for f in ("q4_0_linear.hip", "q4_0_internal.h"):
-        with open(os.path.join(ROOT, "q4_weight_only_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "q4_weight_only_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
