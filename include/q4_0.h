@@ -99,6 +99,15 @@ size_t q4_0_packed_bytes(int64_t N, int64_t K);   /* 0 if N or K is invalid */
  */
 q4_status q4_0_quantize(const float *w, int64_t N, int64_t K, void *gguf_blocks, void *stream);
 
+/*
+ * The same quantizer for bf16 weights (bit patterns, row-major [N, K] on the
+ * device, 16-byte aligned): each value is widened to fp32 exactly (its bits
+ * shifted into the top half) and the fp32 rule above applies unchanged, so
+ * the result equals q4_0_quantize of the widened matrix byte for byte.
+ * Validation and errors as for q4_0_quantize.
+ */
+q4_status q4_0_quantize_bf16(const void *w_bf16, int64_t N, int64_t K, void *gguf_blocks, void *stream);
+
 /* GGUF Q4_0 blocks (device) -> packed layout (device, q4_0_packed_bytes). */
 q4_status q4_0_pack(const void *gguf_blocks, int64_t N, int64_t K, void *packed, void *stream);
 

@@ -255,6 +255,13 @@ def quantize(w: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------- device (packed) layout
+def quantize_bf16(w_bits: np.ndarray) -> np.ndarray:
+    """bf16 W (bit patterns [n, k]) -> GGUF Q4_0 bytes: each value widened to
+    fp32 exactly (bf16 is the top half of an fp32), then the rule of
+    quantize() unchanged."""
+    return quantize(bf16_bits_to_f64(w_bits).astype(np.float32))
+
+
 def padded_dims(n: int, k: int):
     """(Np, Kp): rows rounded up to 16, columns up to 128."""
     return -(-n // TILE_ROWS) * TILE_ROWS, -(-k // TILE_K) * TILE_K

@@ -20,7 +20,7 @@ _lock = threading.Lock()
 Q4_OK = 0
 STATUS_NAMES = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIGN",
                 4: "Q4_ERR_SEGMENTS", 5: "Q4_ERR_HIP"}
-EXPORTS = ("q4_status_str", "q4_0_packed_bytes", "q4_0_quantize", "q4_0_pack", "q4_0_unpack",
+EXPORTS = ("q4_status_str", "q4_0_packed_bytes", "q4_0_quantize", "q4_0_quantize_bf16", "q4_0_pack", "q4_0_unpack",
            "q4_0_dequant", "q4_0_linear", "q4_0_linear_multi", "q4_0_time_next_launch",
            "q4_0_linear_kernel", "q4_0_linear_swiglu", "q4_0_linear_swiglu_kernel", "q4_0_embed")
 
@@ -58,7 +58,7 @@ def lib() -> ctypes.CDLL:
             L.q4_status_str.restype = ctypes.c_char_p
             L.q4_0_packed_bytes.argtypes = [i64, i64]
             L.q4_0_packed_bytes.restype = ctypes.c_size_t
-            for name in ("q4_0_quantize", "q4_0_pack", "q4_0_unpack", "q4_0_dequant"):
+            for name in ("q4_0_quantize", "q4_0_quantize_bf16", "q4_0_pack", "q4_0_unpack", "q4_0_dequant"):
                 fn = getattr(L, name)
                 fn.argtypes = [vp, i64, i64, vp, vp]
                 fn.restype = i32
@@ -125,8 +125,9 @@ class PackedWeight:
 
 
 def quantize(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """fp32 W [N, K] on the device -> GGUF Q4_0 bytes [N, K/32, 18] (uint8)."""
-    _dev(w, "w", torch.float32)
+    """fp32 or bf16 W [N, K] on the device -> GGUF Q4_0 bytes [N, K/32, 18]
+    (uint8); bf16 values are widened to fp32 exactly first."""
+    _dev(w, "w", torch.bfloat16 if w.dtype == torch.bfloat16 else torch.float32)
     if w.dim() != 2:
         raise ValueError("w must be [N, K]")
     n, k = w.shape
@@ -135,8 +136,9 @@ def quantize(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     _dev(out, "out", torch.uint8)
     if out.numel() != gguf_bytes(n, k):
         raise ValueError("out has the wrong size")
+    fn = "q4_0_quantize_bf16" if w.dtype == torch.bfloat16 else "q4_0_quantize"
     with torch.cuda.device(w.device):
-        _check(lib().q4_0_quantize(w.data_ptr(), n, k, out.data_ptr(), _stream(w.device)), "q4_0_quantize")
+        _check(getattr(lib(), fn)(w.data_ptr(), n, k, out.data_ptr(), _stream(w.device)), fn)
     return out
 
 

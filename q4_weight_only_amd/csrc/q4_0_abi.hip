@@ -62,6 +62,14 @@ q4_status q4_0_quantize(const float *w, int64_t N, int64_t K, void *gguf_blocks,
     return from_hip(q4::launch_quantize(w, N, K, static_cast<uint8_t *>(gguf_blocks), as_stream(stream)));
 }
 
+q4_status q4_0_quantize_bf16(const void *w_bf16, int64_t N, int64_t K, void *gguf_blocks, void *stream) {
+    if (!shape_ok(N, K)) return Q4_ERR_SHAPE;
+    if (!w_bf16 || !gguf_blocks) return Q4_ERR_NULL;
+    if (!aligned16(w_bf16) || !aligned16(gguf_blocks)) return Q4_ERR_ALIGN;
+    return from_hip(q4::launch_quantize_bf16(static_cast<const uint16_t *>(w_bf16), N, K,
+                                             static_cast<uint8_t *>(gguf_blocks), as_stream(stream)));
+}
+
 q4_status q4_0_pack(const void *gguf_blocks, int64_t N, int64_t K, void *packed, void *stream) {
     if (!shape_ok(N, K)) return Q4_ERR_SHAPE;
     if (!gguf_blocks || !packed) return Q4_ERR_NULL;

@@ -48,20 +48,37 @@ __device__ inline void store_gguf_block(uint8_t *p, uint16_t d, const uint8_t q[
 // --------------------------------------------------------------- quantize
 // One thread per GGUF block (row n, block b); the block's 32 floats are
 // contiguous at w + (n * K + 32 b), i.e. at w + 32 * (n * K/32 + b).
-__global__ __launch_bounds__(kThreads) void quantize_kernel(const float *__restrict__ w,
+// T is float (fp32 weights) or uint16_t (bf16 bit patterns, widened to fp32
+// exactly by a 16-bit shift before the same rule).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(const T *__restrict__ w,
                                                             int64_t nblocks,
                                                             uint8_t *__restrict__ out) {
     const int64_t idx = blockIdx.x * (int64_t)kThreads + threadIdx.x;
     if (idx >= nblocks) return;
-    const float4 *src = reinterpret_cast<const float4 *>(w + idx * kQK);
     float v[32];
+    if constexpr (sizeof(T) == 4) {
+        const float4 *src = reinterpret_cast<const float4 *>(w + idx * kQK);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const float4 f = src[t];
-        v[4 * t] = f.x;
-        v[4 * t + 1] = f.y;
-        v[4 * t + 2] = f.z;
-        v[4 * t + 3] = f.w;
+        for (int t = 0; t < 8; ++t) {
+            const float4 f = src[t];
+            v[4 * t] = f.x;
+            v[4 * t + 1] = f.y;
+            v[4 * t + 2] = f.z;
+            v[4 * t + 3] = f.w;
+        }
+    } else {
+        const uint4 *src = reinterpret_cast<const uint4 *>(w + idx * kQK);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint4 u = src[t];
+            const uint32_t words[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                v[8 * t + 2 * h] = __uint_as_float(words[h] << 16);
+                v[8 * t + 2 * h + 1] = __uint_as_float(words[h] & 0xFFFF0000u);
+            }
+        }
     }
     // signed element of largest magnitude; strict '>' keeps the first one
     float amax = v[0];
@@ -242,7 +259,15 @@ hipError_t launch_quantize(const float *w, int64_t N, int64_t K, uint8_t *out, h
     const int64_t nblocks = N * (K / kQK);
     dim3 grid;
     if (!grid_for(nblocks, grid)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(quantize_kernel, grid, dim3(kThreads), 0, s, w, nblocks, out);
+    hipLaunchKernelGGL(quantize_kernel<float>, grid, dim3(kThreads), 0, s, w, nblocks, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_bf16(const uint16_t *w, int64_t N, int64_t K, uint8_t *out, hipStream_t s) {
+    const int64_t nblocks = N * (K / kQK);
+    dim3 grid;
+    if (!grid_for(nblocks, grid)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quantize_kernel<uint16_t>, grid, dim3(kThreads), 0, s, w, nblocks, out);
     return hipGetLastError();
 }
 

@@ -50,6 +50,7 @@ struct LinearArgs {
 
 // Launchers (return hipError_t from the launch).
 hipError_t launch_quantize(const float *w, int64_t N, int64_t K, uint8_t *out, hipStream_t s);
+hipError_t launch_quantize_bf16(const uint16_t *w, int64_t N, int64_t K, uint8_t *out, hipStream_t s);
 hipError_t launch_pack(const uint8_t *gguf, int64_t N, int64_t K, uint8_t *packed, hipStream_t s);
 hipError_t launch_unpack(const uint8_t *packed, int64_t N, int64_t K, uint8_t *gguf, hipStream_t s);
 hipError_t launch_dequant(const uint8_t *packed, int64_t N, int64_t K, float *w, hipStream_t s);

@@ -62,7 +62,7 @@ def test_packed_bytes_invalid_is_zero(L, n, k):
     assert q4.packed_bytes(n, k) == 0
 
 
-@pytest.mark.parametrize("fn", ["q4_0_quantize", "q4_0_pack", "q4_0_unpack", "q4_0_dequant"])
+@pytest.mark.parametrize("fn", ["q4_0_quantize", "q4_0_quantize_bf16", "q4_0_pack", "q4_0_unpack", "q4_0_dequant"])
 def test_format_entry_points_validate_first(L, fn):
     f = getattr(L, fn)
     assert f(FAKE, 16, 48, FAKE, None) == SHAPE
@@ -181,6 +181,7 @@ def test_format_grids_beyond_the_limit_are_refused(L):
     HIP = 5
     n, k = 2**30, 2**20
     assert L.q4_0_quantize(FAKE, n, k, FAKE, None) == HIP
+    assert L.q4_0_quantize_bf16(FAKE, n, k, FAKE, None) == HIP
     assert L.q4_0_pack(FAKE, n, k, FAKE, None) == HIP
     assert L.q4_0_unpack(FAKE, n, k, FAKE, None) == HIP
     assert L.q4_0_dequant(FAKE, n, k, FAKE, None) == HIP

@@ -1,5 +1,5 @@
 """Bit-exact checks of the device format kernels against the oracle:
-quantize (fp32 -> GGUF), pack (GGUF -> tiled), unpack (inverse), dequant."""
+quantize (fp32 or bf16 -> GGUF), pack (GGUF -> tiled), unpack (inverse), dequant."""
 
 import numpy as np
 import pytest
@@ -50,6 +50,18 @@ def test_quantize_structured_blocks():
     say("quantize structured", w.shape)
     got = q4.quantize(torch.from_numpy(np.ascontiguousarray(w)).to(DEV)).cpu().numpy()
     assert np.array_equal(got, O.quantize(w))
+
+
+@pytest.mark.parametrize("n,k", SHAPES)
+def test_quantize_bf16_matches_oracle_bytes(n, k):
+    """bf16 weights: the oracle's rule on the exactly widened values, and the
+    same bytes as the fp32 quantizer given those widened values."""
+    w = inputs.bf16_bits_from_f32(inputs.weights_f32((n, k), seed=12, tags=(n, k)))
+    wt = torch.from_numpy(w.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
+    say("quantize bf16", n, k)
+    got = q4.quantize(wt).cpu().numpy()
+    assert np.array_equal(got, O.quantize_bf16(w))
+    assert np.array_equal(got, q4.quantize(wt.float()).cpu().numpy())
 
 
 @pytest.mark.parametrize("n,k", SHAPES)

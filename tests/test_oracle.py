@@ -250,6 +250,23 @@ def test_quantizer_positive_extreme_by_hand():
     assert q[:3] == [7, 11, 0]
 
 
+def test_bf16_quantizer_by_hand():
+    # bf16 0xBF80 = -1.0, 0x3F00 = 0.5, 0x3E80 = 0.25, 0xBE80 = -0.25,
+    # 0x3E00 = 0.125: the negative-extreme block above, entered as bf16 bits
+    bits = np.zeros((1, 32), dtype=np.uint16)
+    bits[0, :5] = [0xBF80, 0x3F00, 0x3E80, 0xBE80, 0x3E00]
+    blk = O.quantize_bf16(bits)
+    d, q = O.gguf_decode(blk, 1, 32)
+    assert d.view(np.uint16)[0, 0] == 0x3000
+    assert list(q[0, :5]) == [0, 12, 10, 6, 9] and list(q[0, 5:]) == [8] * 27
+    # bf16 0x3DCD = 0.10009765625: with the other values, the widened block
+    # quantizes as its fp32 twin does (a byte-swapped or shifted widening fails)
+    bits[0, 5] = 0x3DCD
+    w = np.zeros((1, 32), dtype=np.float32)
+    w[0, :6] = [-1.0, 0.5, 0.25, -0.25, 0.125, 0.10009765625]
+    assert np.array_equal(O.quantize_bf16(bits), O.quantize(w))
+
+
 def test_quantizer_ties_round_half_to_even():
     # amax = -2 -> d = 0.25; 0.625/0.25 = 2.5 -> 2; 0.875/0.25 = 3.5 -> 4;
     # -0.375/0.25 = -1.5 -> -2; 0.125/0.25 = 0.5 -> 0
