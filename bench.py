@@ -28,6 +28,9 @@ Printed (one JSON line):
               after a 512 MiB read (rows from HBM), and GB/s moved
   lm_head     the same table as the LM head linear at M = 1 and 32 (kernel-own
               times, each launch after a 512 MiB read so the table comes from HBM)
+  other_workloads  the lone GEMV 3072->4096 at M=1 and the audio linears
+              (5120->3072 and 3072->3072 at M=1505, 1280->5120 and 5120->1280
+              at M=6020), timed like the LM head: median, p10 and p90
   cpu_baseline  the CPU oracle (dequantize + fp64 matmul) on a bounded sample
               of the same step, on the host cores
 """
@@ -68,6 +71,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-swiglu", action="store_true", help="skip the fused gate/up + SwiGLU timings")
     p.add_argument("--no-embed", action="store_true", help="skip the Q4 embedding lookup timings")
+    p.add_argument("--no-others", action="store_true",
+                   help="skip the single GEMV and the audio linears (M = 1505, 6020)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 256 MiB device copy (reference kernel for PMC byte counters)")
@@ -162,7 +167,8 @@ class Runner:
 
 
 def time_graph(runner, steps, warmup, dev):
-    """Capture one step in a HIP graph; time `steps` replays with events."""
+    """Capture one step in a HIP graph; time `steps` replays with events (one
+    between every two replays, so each step's time is kept too)."""
     import torch
 
     stream = torch.cuda.Stream(dev)
@@ -177,15 +183,21 @@ def time_graph(runner, steps, warmup, dev):
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             graph.replay()
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         torch.cuda.synchronize(dev)
-        start.record(stream)
-        for _ in range(steps):
+        marks[0].record(stream)
+        for i in range(steps):
             graph.replay()
-        stop.record(stream)
-    stop.synchronize()
-    return start.elapsed_time(stop) / 1e3, graph
+            marks[i + 1].record(stream)
+    marks[-1].synchronize()
+    runner.step_times = [marks[i].elapsed_time(marks[i + 1]) / 1e3 for i in range(steps)]
+    return marks[0].elapsed_time(marks[-1]) / 1e3, graph
+
+
+def pctl_us(times):
+    import numpy as np
+
+    return [round(float(np.percentile(times, q)) * 1e6, 2) for q in (10, 50, 90)]
 
 
 def time_kernels(runner, steps, dev):
@@ -310,11 +322,12 @@ def time_embed(pw, counts, reps, dev):
     return out
 
 
-def time_lm_head(spec, pw, ms, reps, dev):
-    """The 131072 x 3072 LM head as a single linear at each M: kernel-own time
-    (armed events) of launches that each follow a read of a 512 MiB buffer,
-    so the table streams from HBM rather than from the 256 MB infinity cache
-    (a read, not a fill, so no write-back competes with the launch)."""
+def time_single(spec, pw, ms, reps, dev):
+    """One single-segment linear at each M: kernel-own time (armed events) of
+    launches that each follow a read of a 512 MiB buffer, so the weights
+    stream from HBM rather than from the 256 MB infinity cache (a read, not
+    a fill, so no write-back competes with the launch).  Median and
+    p10 / p90 over `reps` launches after one warm-up launch."""
     import numpy as np
     import torch
 
@@ -340,11 +353,17 @@ def time_lm_head(spec, pw, ms, reps, dev):
             q4.linear(x, pw, y)
             pairs.append((a, b))
         torch.cuda.synchronize(dev)
-        t = float(np.median([a.elapsed_time(b) / 1e3 for a, b in pairs]))
+        ts = np.array([a.elapsed_time(b) / 1e3 for a, b in pairs])
+        t = float(np.median(ts))
         moved = algorithmic_bytes(spec, m)
         out[f"M={m}"] = {"kernel": q4.linear_kernel(m, spec.K, spec.Ns), "us": round(t * 1e6, 2),
+                         "p10_us": round(float(np.percentile(ts, 10)) * 1e6, 2),
+                         "p90_us": round(float(np.percentile(ts, 90)) * 1e6, 2),
                          "GBs": round(moved / t / 1e9, 1), "frac_of_8TBs": round(moved / t / 1e9 / HBM_PEAK_GBS, 4),
-                         "TFLOPs": round(flops(spec, m) / t / 1e12, 2), "launches": reps}
+                         "TFLOPs": round(flops(spec, m) / t / 1e12, 2),
+                         "frac_of_bf16_peak": round(flops(spec, m) / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "launches": reps}
+        del x, y
     del flush, sink
     return out
 
@@ -456,11 +475,13 @@ def main():
     # group launches by the kernel instantiation that ran them
     by_kernel = collections.OrderedDict()
     per_op = collections.OrderedDict()
+    per_op_times = {}
     for (spec, *_), d in zip(runner.items, durations):
         kname = q4.linear_kernel(1, spec.K, spec.Ns)
         b, t, c = by_kernel.get(kname, (0, 0.0, 0))
         by_kernel[kname] = (b + algorithmic_bytes(spec, 1) * len(d), t + sum(d), c + len(d))
         op = spec.name.split(".", 1)[1]
+        per_op_times.setdefault(op, []).extend(d)
         b, t, c = per_op.get(op, (0, 0.0, 0))
         per_op[op] = (b + algorithmic_bytes(spec, 1) * len(d), t + sum(d), c + len(d))
     dominant = max(by_kernel, key=lambda k: by_kernel[k][1])
@@ -482,6 +503,7 @@ def main():
                     for k, (b, t, c) in by_kernel.items()},
         "per_op_GBs": {op: round(b / t / 1e9, 1) for op, (b, t, c) in per_op.items()},
         "per_op_avg_us": {op: round(t / c * 1e6, 2) for op, (b, t, c) in per_op.items()},
+        "per_op_p10_p50_p90_us": {op: pctl_us(v) for op, v in per_op_times.items()},
     }
     log(f"dominant decode kernel {dominant}: {achieved:.1f} GB/s over {launches} launches; per op {roofline['per_op_GBs']}")
 
@@ -493,6 +515,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "step_us_p10_p50_p90": pctl_us(runner.step_times),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -518,6 +541,7 @@ def main():
     out["decode_m2"] = {
         "workload": "the decode step at M=2 (batched CFG pair), same weights and launches",
         "us_per_step": round(el2 / args.steps * 1e6, 1),
+        "step_us_p10_p50_p90": pctl_us(runner2.step_times),
         "value": round(gbs2, 1),
         "unit": "GB/s",
         "frac_of_8TBs": round(gbs2 / HBM_PEAK_GBS, 4),
@@ -556,6 +580,7 @@ def main():
             "unit": "TFLOP/s",
             "workload": "M=2048 through QKV 3072->6144, O 4096->3072, gate/up 3072->18432, down 9216->3072",
             "ms_per_step": round(pel / args.prefill_steps * 1e3, 4),
+            "step_us_p10_p50_p90": pctl_us(prunner.step_times),
             "steps": args.prefill_steps,
             "roofline": {
                 "bound": "mfma",
@@ -593,10 +618,25 @@ def main():
         # the same table as the LM head linear (workload 3: M = 1 and 32)
         out["lm_head"] = {
             "workload": f"LM head {lm_spec.K}->{lm_spec.Ns[0]} (226 MB of Q4_0), one launch, streamed from HBM",
-            **time_lm_head(lm_spec, lm_pws[0], (1, 32), 20, dev),
+            **time_single(lm_spec, lm_pws[0], (1, 32), 20, dev),
         }
         log(f"lm_head: {out['lm_head']}")
         del lm_pws
+
+    # ---- the other workloads' single launches: the lone GEMV and the audio
+    # linears (ragged M = 1505 and 6020), each from HBM
+    if not args.no_others:
+        _, g1 = inputs.workload(1)
+        _, a5 = inputs.workload(5)
+        others = {}
+        for spec, ms in g1 + a5:
+            (_, pws, _), = build_device_specs([spec], (), dev)
+            res = time_single(spec, pws[0], ms, 20, dev)
+            for key, r in res.items():
+                others[f"{spec.name} {spec.K}->{spec.Ns[0]} {key}"] = r
+            del pws
+        out["other_workloads"] = others
+        log(f"other workloads: {others}")
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
