@@ -21,7 +21,13 @@
  * Conventions for every entry point.
  *   - Pointers named as device memory must be device (or managed) memory on
  *     the current HIP device; the caller owns every buffer.  The library
- *     allocates nothing and keeps no state between calls.
+ *     allocates no device memory and keeps no data between calls: only
+ *     per-device caches of the CU count and kernel occupancy, and the
+ *     per-kernel LDS limits it raises once with hipFuncSetAttribute.
+ *   - Output buffers must not overlap any input of the same call, nor each
+ *     other; inputs may be shared freely, also by concurrent calls.
+ *   - Entry points may be called from several host threads at once.  The
+ *     timing hook (q4_0_time_next_launch) affects the calling thread only.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Every call that
  *     launches work is asynchronous on that stream; results are visible after
  *     the caller synchronizes it.
