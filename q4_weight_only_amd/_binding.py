@@ -102,6 +102,11 @@ def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _same_device(t: torch.Tensor, other: torch.Tensor, name: str) -> None:
+    if t.device != other.device:
+        raise ValueError(f"{name} is on {other.device}, not {t.device}")
+
+
 # ------------------------------------------------------------------ API
 def packed_bytes(n: int, k: int) -> int:
     return int(lib().q4_0_packed_bytes(int(n), int(k)))
@@ -136,6 +141,7 @@ def quantize(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     _dev(out, "out", torch.uint8)
     if out.numel() != gguf_bytes(n, k):
         raise ValueError("out has the wrong size")
+    _same_device(w, out, "out")
     fn = "q4_0_quantize_bf16" if w.dtype == torch.bfloat16 else "q4_0_quantize"
     with torch.cuda.device(w.device):
         _check(getattr(lib(), fn)(w.data_ptr(), n, k, out.data_ptr(), _stream(w.device)), fn)
@@ -155,6 +161,7 @@ def pack(blocks: torch.Tensor, n: int, k: int, out: torch.Tensor | None = None) 
     _dev(out, "out", torch.uint8)
     if out.numel() != nbytes:
         raise ValueError("out has the wrong size")
+    _same_device(blocks, out, "out")
     with torch.cuda.device(blocks.device):
         _check(lib().q4_0_pack(blocks.data_ptr(), n, k, out.data_ptr(), _stream(blocks.device)), "q4_0_pack")
     return PackedWeight(out, n, k)
@@ -187,6 +194,8 @@ def embed(pw: PackedWeight, ids: torch.Tensor, out: torch.Tensor | None = None) 
     _dev(out, "out", torch.float32)
     if tuple(out.shape) != (ids.shape[0], pw.k):
         raise ValueError("out has the wrong shape")
+    _same_device(ids, pw.data, "the table")
+    _same_device(ids, out, "out")
     with torch.cuda.device(ids.device):
         _check(lib().q4_0_embed(pw.data.data_ptr(), pw.n, pw.k, ids.data_ptr(), ids.shape[0], out.data_ptr(),
                                 _stream(ids.device)), "q4_0_embed")
@@ -204,6 +213,8 @@ def linear(x: torch.Tensor, pw: PackedWeight, out: torch.Tensor | None = None) -
     _dev(out, "out", torch.float32)
     if tuple(out.shape) != (m, pw.n):
         raise ValueError("out has the wrong shape")
+    _same_device(x, pw.data, "the weights")
+    _same_device(x, out, "out")
     with torch.cuda.device(x.device):
         _check(lib().q4_0_linear(x.data_ptr(), m, pw.data.data_ptr(), pw.n, pw.k, out.data_ptr(),
                                  _stream(x.device)), "q4_0_linear")
@@ -213,6 +224,8 @@ def linear(x: torch.Tensor, pw: PackedWeight, out: torch.Tensor | None = None) -
 def linear_multi(x: torch.Tensor, weights, outs=None):
     """One launch over several weight matrices sharing x: returns [y_i]."""
     _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
     weights = list(weights)
     if not 1 <= len(weights) <= 8:
         raise ValueError("need 1..8 weight matrices")
@@ -220,6 +233,9 @@ def linear_multi(x: torch.Tensor, weights, outs=None):
     m = x.shape[0]
     if outs is None:
         outs = [torch.empty((m, w.n), dtype=torch.float32, device=x.device) for w in weights]
+    outs = list(outs)
+    if len(outs) != len(weights):
+        raise ValueError(f"{len(weights)} weight matrices but {len(outs)} outputs")
     segs = (Segment * len(weights))()
     for i, (w, y) in enumerate(zip(weights, outs)):
         if w.k != k:
@@ -227,6 +243,8 @@ def linear_multi(x: torch.Tensor, weights, outs=None):
         _dev(y, f"outs[{i}]", torch.float32)
         if tuple(y.shape) != (m, w.n):
             raise ValueError(f"outs[{i}] has the wrong shape")
+        _same_device(x, w.data, f"weights[{i}]")
+        _same_device(x, y, f"outs[{i}]")
         segs[i] = Segment(w.data.data_ptr(), w.n, y.data_ptr())
     with torch.cuda.device(x.device):
         _check(lib().q4_0_linear_multi(x.data_ptr(), m, k, segs, len(weights), _stream(x.device)),
@@ -251,6 +269,9 @@ def linear_swiglu(x: torch.Tensor, gate: PackedWeight, up: PackedWeight,
     _dev(out, "out", dtype)
     if tuple(out.shape) != (m, gate.n):
         raise ValueError("out has the wrong shape")
+    _same_device(x, gate.data, "gate")
+    _same_device(x, up.data, "up")
+    _same_device(x, out, "out")
     with torch.cuda.device(x.device):
         _check(lib().q4_0_linear_swiglu(x.data_ptr(), m, gate.k, gate.data.data_ptr(), up.data.data_ptr(),
                                         gate.n, out.data_ptr(), int(dtype == torch.bfloat16), _stream(x.device)),

@@ -156,3 +156,17 @@ def test_m_zero_is_a_no_op():
     assert q4.lib().q4_0_linear(x.data_ptr(), 0, pw.data.data_ptr(), n, k, sentinel.data_ptr(), None) == 0
     torch.cuda.synchronize()
     assert torch.all(sentinel == 7.0)
+
+
+def test_binding_rejects_mismatched_arguments():
+    n, k, m = 32, 64, 2
+    pw, _ = device_weight_from_f32(inputs.weights_f32((n, k), seed=5))
+    x = to_dev_x(inputs.activations_bf16((m, k), seed=5))
+    say("binding validation")
+    with pytest.raises(ValueError, match="outputs"):
+        q4.linear_multi(x, [pw, pw], [torch.empty((m, n), device=DEV)])
+    with pytest.raises(ValueError, match=r"\[M, K\]"):
+        q4.linear_multi(x.view(-1), [pw])
+    with pytest.raises(ValueError, match="CUDA/HIP"):
+        q4.linear(x, pw, out=torch.empty((m, n)))
+    torch.cuda.synchronize()
