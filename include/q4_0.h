@@ -42,6 +42,9 @@
  *     N * K/32 * 18 bytes, contiguous.
  *   - Sizes: 1 <= N <= 2^30, 32 <= K <= 2^20, K % 32 == 0, 0 <= M <= 2^20.
  *     M == 0 is a successful no-op.
+ *   - NaN or +-inf in x or in a scale d: an output is non-finite exactly
+ *     where sum_k x[m,k] * ((q-8) * d) is (inf rather than NaN is possible
+ *     when d is infinite, since d scales each 32-block's sum).
  */
 #ifndef Q4_0_H
 #define Q4_0_H

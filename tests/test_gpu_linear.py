@@ -170,3 +170,38 @@ def test_binding_rejects_mismatched_arguments():
     with pytest.raises(ValueError, match="CUDA/HIP"):
         q4.linear(x, pw, out=torch.empty((m, n)))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("m", [1, 3, 40, 130])
+def test_non_finite_inputs_stay_non_finite_where_the_definition_is(m):
+    """NaN / inf in x or in a scale d: an output is non-finite exactly where
+    the dequantize-then-matmul definition's is, and every finite output is
+    within the bound.  (With d = +-inf the kinds can differ: the kernel scales
+    the block sum sum_k x (q - 8), the definition each weight (q - 8) d, so
+    a zero x next to a nonzero code gives NaN there and +-inf here.)"""
+    n, k = 80, 320
+    blocks = O.quantize(inputs.weights_f32((n, k), seed=21)).copy()
+    d_bits = blocks[:, :, :2].view(np.uint16)
+    d_bits[3, 2, 0] = 0x7C00            # +inf
+    d_bits[7, 0, 0] = 0x7E00            # NaN
+    d_bits[9, 5, 0] = 0xFC00            # -inf, on a block of all codes 8 (w = 0 * inf)
+    blocks[9, 5, 2:] = 0x88
+    d_bits[60, 9, 0] = 0x7BFF           # 65504, finite
+    xb = inputs.activations_bf16((m, k), seed=21).copy()
+    if m >= 2:
+        xb[0, 10] = 0x7FC0              # NaN in the first row
+    if m >= 3:
+        xb[m - 1, 100] = 0x7F80         # +inf in the last row
+    pw = device_weight_from_blocks(blocks, n, k)
+    say("non-finite", m)
+    y = q4.linear(to_dev_x(xb), pw).cpu().numpy().astype(np.float64)
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = O.linear(xb, blocks, n, k)
+        bound = O.error_bound(xb, blocks, n, k)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(y), fin)
+    if m >= 2:
+        assert np.all(np.isnan(y[0])), "a NaN in x poisons its whole output row"
+    assert not fin.all() and fin.any()
+    err = np.abs(y[fin] - ref[fin])
+    assert np.all(err <= bound[fin]), float((err / bound[fin]).max())
