@@ -201,3 +201,15 @@ def test_product_path_has_no_oracle_dependency():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 src = open(os.path.join(root, f), encoding="utf-8").read()
                 assert "import oracle" not in src and "from oracle" not in src, f
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    p = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert p.returncode == 2
+    assert "one GPU only" in p.stderr
+    assert p.stdout == ""
