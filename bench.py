@@ -23,9 +23,10 @@ Printed (one JSON line):
               the unfused gate/up launch it replaces, at M = 1, 2 and 2048
               (kernel-own times; each kind walks the 26 layers' gate/up
               weights in turn, so every launch streams its weights from HBM)
-  embed       Q4 embedding lookups (q4_0_embed) of 32, 2048 and 16384 random ids
-              from the 131072 x 3072 table: kernel-own time per launch, each
-              after a 512 MiB read (rows from HBM), and GB/s moved
+  embed       Q4 embedding lookups of 32, 2048 and 16384 random ids from the
+              131072 x 3072 table, packed (q4_0_embed) and as GGUF blocks
+              (q4_0_embed_gguf, under "gguf"): kernel-own time per launch,
+              each after a 512 MiB read (rows from HBM), and GB/s moved
   lm_head     the same table as the LM head linear at M = 1 and 32 (kernel-own
               times, each launch after a 512 MiB read so the table comes from HBM)
   other_workloads  the lone GEMV 3072->4096 at M=1 and the audio linears
@@ -285,11 +286,12 @@ def time_swiglu(prepared, ms, reps, dev):
     return out
 
 
-def time_embed(pw, counts, reps, dev):
+def time_embed(pw, counts, reps, dev, blocks=None):
     """Kernel-own times (armed events) of Q4 embedding lookups, each launch
     with fresh random ids and after a read of a 512 MiB buffer, so the table
     rows come from HBM: the 226 MB table would otherwise sit in the 256 MB
-    infinity cache after the first launches."""
+    infinity cache after the first launches.  With `blocks` (the same table
+    as GGUF bytes) the lookups run q4_0_embed_gguf instead."""
     import numpy as np
     import torch
 
@@ -311,7 +313,10 @@ def time_embed(pw, counts, reps, dev):
             a.record(stream)
             b.record(stream)
             q4.time_next_launch(a, b)
-            q4.embed(pw, batch, res)
+            if blocks is None:
+                q4.embed(pw, batch, res)
+            else:
+                q4.embed_gguf(blocks, pw.n, pw.k, batch, res)
             if r > 0:                      # the first launch warms up
                 pairs.append((a, b))
         torch.cuda.synchronize(dev)
@@ -609,11 +614,17 @@ def main():
     if not args.no_embed:
         _, lm = inputs.workload(3)
         lm_spec = lm[0][0]
-        (_, lm_pws, _), = build_device_specs([lm_spec], (), dev)
+        wt = torch.from_numpy(lm_spec.weight(0)).to(dev)
+        lm_blocks = q4.quantize(wt)
+        del wt
+        lm_pws = [q4.pack(lm_blocks, lm_spec.Ns[0], lm_spec.K)]
         out["embed"] = {
-            "table": f"{lm_spec.Ns[0]}x{lm_spec.K} Q4_0 (the LM head weights), fp32 rows out, random ids",
+            "table": f"{lm_spec.Ns[0]}x{lm_spec.K} Q4_0 (the LM head weights), fp32 rows out, random ids; "
+                     "packed table (q4_0_embed) and GGUF block order (q4_0_embed_gguf, key gguf)",
             **time_embed(lm_pws[0], (32, 2048, 16384), 50, dev),
+            "gguf": time_embed(lm_pws[0], (32, 2048, 16384), 50, dev, blocks=lm_blocks),
         }
+        del lm_blocks
         log(f"embed: {out['embed']}")
         # the same table as the LM head linear (workload 3: M = 1 and 32)
         out["lm_head"] = {

@@ -141,6 +141,18 @@ q4_status q4_0_embed(const void *packed, int64_t N, int64_t K, const int32_t *id
                      float *out, void *stream);
 
 /*
+ * The same lookup on a table kept as GGUF Q4_0 blocks ([N, K/32, 18] bytes,
+ * device, 16-byte aligned), where one row's blocks are contiguous.  A lookup
+ * then reads only its rows' K/32 * 18 bytes; in the packed layout a row is
+ * 16-byte pieces 256 bytes apart, and each piece costs a whole cache line
+ * (about 9x the row's bytes measured from HBM).  Same result as q4_0_embed
+ * on the packed form of the same table, bit for bit (NaN rows for bad ids);
+ * same validation and limits.
+ */
+q4_status q4_0_embed_gguf(const void *gguf_blocks, int64_t N, int64_t K, const int32_t *ids, int64_t n_ids,
+                          float *out, void *stream);
+
+/*
  * y[M, N] (fp32, device) = x[M, K] (bf16, device) times W^T, W packed.
  * Accuracy: every product (q - 8) * x is formed exactly and scaled by d in
  * fp32; y is within 1e-3 * sum_k |x_k * w_k| + 1e-6 of the exact result for
@@ -215,7 +227,8 @@ const char *q4_0_linear_kernel(int64_t M, int64_t K, const int64_t *N, int nseg)
 
 /*
  * Measurement hook for benchmarks.  Arms the calling thread's next
- * q4_0_linear / q4_0_linear_multi / q4_0_linear_swiglu / q4_0_embed launch so that its kernel records
+ * q4_0_linear / q4_0_linear_multi / q4_0_linear_swiglu / q4_0_embed / q4_0_embed_gguf launch so that
+ * its kernel records
  * `start_event` when it starts executing and `stop_event` when it finishes
  * (hipExtLaunchKernelGGL); hipEventElapsedTime on the pair is then that
  * kernel's own duration, without launch gaps -- the quantity a kernel trace

@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     Q4Error,
     dequant,
     embed,
+    embed_gguf,
     gguf_bytes,
     lib,
     library_path,

@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIG
                 4: "Q4_ERR_SEGMENTS", 5: "Q4_ERR_HIP"}
 EXPORTS = ("q4_status_str", "q4_0_packed_bytes", "q4_0_quantize", "q4_0_quantize_bf16", "q4_0_pack", "q4_0_unpack",
            "q4_0_dequant", "q4_0_linear", "q4_0_linear_multi", "q4_0_time_next_launch",
-           "q4_0_linear_kernel", "q4_0_linear_swiglu", "q4_0_linear_swiglu_kernel", "q4_0_embed")
+           "q4_0_linear_kernel", "q4_0_linear_swiglu", "q4_0_linear_swiglu_kernel", "q4_0_embed",
+           "q4_0_embed_gguf")
 
 
 class Q4Error(ValueError):
@@ -62,8 +63,10 @@ def lib() -> ctypes.CDLL:
                 fn = getattr(L, name)
                 fn.argtypes = [vp, i64, i64, vp, vp]
                 fn.restype = i32
-            L.q4_0_embed.argtypes = [vp, i64, i64, vp, i64, vp, vp]
-            L.q4_0_embed.restype = i32
+            for name in ("q4_0_embed", "q4_0_embed_gguf"):
+                fn = getattr(L, name)
+                fn.argtypes = [vp, i64, i64, vp, i64, vp, vp]
+                fn.restype = i32
             L.q4_0_linear.argtypes = [vp, i64, vp, i64, i64, vp, vp]
             L.q4_0_linear.restype = i32
             L.q4_0_linear_multi.argtypes = [vp, i64, i64, ctypes.POINTER(Segment), i32, vp]
@@ -202,6 +205,30 @@ def embed(pw: PackedWeight, ids: torch.Tensor, out: torch.Tensor | None = None) 
     return out
 
 
+def embed_gguf(blocks: torch.Tensor, n: int, k: int, ids: torch.Tensor,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """Rows ids of a table kept as GGUF Q4_0 bytes (uint8, N*K/32*18 elements,
+    on the device), dequantized: [len(ids), K] fp32, equal to embed() on the
+    packed form of the same table."""
+    _dev(blocks, "blocks", torch.uint8)
+    if blocks.numel() != gguf_bytes(n, k):
+        raise ValueError(f"blocks must hold {gguf_bytes(n, k)} bytes for [{n}, {k}]")
+    _dev(ids, "ids", torch.int32)
+    if ids.dim() != 1:
+        raise ValueError("ids must be 1-D")
+    if out is None:
+        out = torch.empty((ids.shape[0], int(k)), dtype=torch.float32, device=ids.device)
+    _dev(out, "out", torch.float32)
+    if tuple(out.shape) != (ids.shape[0], int(k)):
+        raise ValueError("out has the wrong shape")
+    _same_device(ids, blocks, "the table")
+    _same_device(ids, out, "out")
+    with torch.cuda.device(ids.device):
+        _check(lib().q4_0_embed_gguf(blocks.data_ptr(), int(n), int(k), ids.data_ptr(), ids.shape[0],
+                                     out.data_ptr(), _stream(ids.device)), "q4_0_embed_gguf")
+    return out
+
+
 def linear(x: torch.Tensor, pw: PackedWeight, out: torch.Tensor | None = None) -> torch.Tensor:
     """y [M, N] fp32 = x [M, K] bf16 times W^T."""
     _dev(x, "x", torch.bfloat16)
@@ -280,7 +307,7 @@ def linear_swiglu(x: torch.Tensor, gate: PackedWeight, up: PackedWeight,
 
 
 def time_next_launch(start: "torch.cuda.Event", stop: "torch.cuda.Event") -> None:
-    """Arm this thread's next linear, SwiGLU or embedding launch to record
+    """Arm this thread's next linear, SwiGLU or embedding (either table form) launch to record
     start/stop at its kernel's own start and end (events must already exist:
     record them once first)."""
     _check(lib().q4_0_time_next_launch(start.cuda_event, stop.cuda_event), "q4_0_time_next_launch")

@@ -103,6 +103,16 @@ q4_status q4_0_embed(const void *packed, int64_t N, int64_t K, const int32_t *id
                                      as_stream(stream)));
 }
 
+q4_status q4_0_embed_gguf(const void *gguf_blocks, int64_t N, int64_t K, const int32_t *ids, int64_t n_ids,
+                          float *out, void *stream) {
+    if (!shape_ok(N, K) || n_ids < 0 || n_ids > (int64_t(1) << 24)) return Q4_ERR_SHAPE;
+    if (n_ids == 0) return Q4_OK;
+    if (!gguf_blocks || !ids || !out) return Q4_ERR_NULL;
+    if (!aligned16(gguf_blocks) || !aligned16(out) || (reinterpret_cast<uintptr_t>(ids) & 3u)) return Q4_ERR_ALIGN;
+    return from_hip(q4::launch_embed_gguf(static_cast<const uint8_t *>(gguf_blocks), N, K, ids, n_ids, out,
+                                          as_stream(stream)));
+}
+
 q4_status q4_0_linear(const void *x_bf16, int64_t M, const void *packed, int64_t N, int64_t K, float *y,
                       void *stream) {
     q4_0_segment seg;

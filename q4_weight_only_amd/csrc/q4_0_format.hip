@@ -253,6 +253,62 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(const uint8_t *__restri
     }
 }
 
+// ---------------------------------------------------------- embed (GGUF)
+// The same lookup on a table kept in GGUF block order, where one row's
+// blocks are contiguous (K/32 * 18 bytes): a lookup reads only the bytes of
+// its rows, whereas in the tiled layout a row is 16-byte pieces 256 bytes
+// apart and every piece costs a whole cache line.  A work unit is (id, run
+// of up to kEmbedRunBlocks blocks); the workgroup copies the run's bytes
+// into LDS with coalesced 2-byte loads (a row start is only 2-byte aligned)
+// and writes the outputs as consecutive float4 stores, nontemporal (the rows
+// are written once and not read back here; 8% faster at 16384 ids).  The two
+// LDS buffers alternate between units, so one barrier per unit suffices.
+constexpr int kEmbedRunBlocks = 256;
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kThreads) void embed_gguf_kernel(const uint16_t *__restrict__ table, int32_t N,
+                                                              int32_t K, const int32_t *__restrict__ ids,
+                                                              int64_t units, int32_t runs,
+                                                              float *__restrict__ out) {
+    __shared__ uint16_t buf[2][kEmbedRunBlocks * 9];
+    const int nb = K / kQK;
+    int parity = 0;
+    for (int64_t u = blockIdx.x; u < units; u += gridDim.x, parity ^= 1) {
+        const int64_t row = u / runs;
+        const int b0 = static_cast<int>(u - row * runs) * kEmbedRunBlocks;
+        const int nbr = nb - b0 < kEmbedRunBlocks ? nb - b0 : kEmbedRunBlocks;
+        const int32_t id = ids[row];
+        const bool ok = id >= 0 && id < N;   // uniform over the workgroup
+        uint16_t *sb = buf[parity];
+        if (ok) {
+            const uint16_t *src = table + (static_cast<int64_t>(id) * nb + b0) * 9;
+            for (int j = threadIdx.x; j < nbr * 9; j += kThreads) sb[j] = src[j];
+        }
+        __syncthreads();
+        float4v *dst = reinterpret_cast<float4v *>(out + row * K + static_cast<int64_t>(b0) * kQK);
+        for (int q = threadIdx.x; q < nbr * 8; q += kThreads) {
+            const int b = q >> 3, e = (q & 7) * 4;   // elements e .. e+3 of block b
+            float4v v;
+            if (ok) {
+                const float d = __half2float(__ushort_as_half(sb[b * 9]));
+                // code bytes 2 + (e mod 16) .. +3: elements e < 16 in the low
+                // nibbles, e >= 16 in the high nibbles of the same bytes
+                const int h = b * 9 + 1 + ((e & 15) >> 1);
+                const uint32_t bytes = sb[h] | (static_cast<uint32_t>(sb[h + 1]) << 16);
+                const int sh = e < 16 ? 0 : 4;
+                v.x = static_cast<float>(static_cast<int>((bytes >> sh) & 15u) - 8) * d;
+                v.y = static_cast<float>(static_cast<int>((bytes >> (8 + sh)) & 15u) - 8) * d;
+                v.z = static_cast<float>(static_cast<int>((bytes >> (16 + sh)) & 15u) - 8) * d;
+                v.w = static_cast<float>(static_cast<int>((bytes >> (24 + sh)) & 15u) - 8) * d;
+            } else {
+                const float nan = __builtin_nanf("");
+                v = (float4v){nan, nan, nan, nan};
+            }
+            __builtin_nontemporal_store(v, dst + q);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const float *w, int64_t N, int64_t K, uint8_t *out, hipStream_t s) {
@@ -319,6 +375,22 @@ hipError_t launch_embed(const uint8_t *packed, int64_t N, int64_t K, const int32
     else
         hipLaunchKernelGGL(embed_kernel, grid, dim3(kThreads), 0, s, packed, scales, (int32_t)N, (int32_t)K,
                            (int32_t)pd.KT, ids, total, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_embed_gguf(const uint8_t *gguf, int64_t N, int64_t K, const int32_t *ids, int64_t n_ids,
+                             float *out, hipStream_t s) {
+    const int32_t runs = static_cast<int32_t>((K / kQK + kEmbedRunBlocks - 1) / kEmbedRunBlocks);
+    const int64_t units = n_ids * runs;
+    const dim3 grid(static_cast<uint32_t>(units < 65536 ? units : 65536));
+    const uint16_t *table = reinterpret_cast<const uint16_t *>(gguf);
+    hipEvent_t start = nullptr, stop = nullptr;
+    if (take_launch_events(start, stop))
+        hipExtLaunchKernelGGL(embed_gguf_kernel, grid, dim3(kThreads), 0, s, start, stop, 0, table, (int32_t)N,
+                              (int32_t)K, ids, units, runs, out);
+    else
+        hipLaunchKernelGGL(embed_gguf_kernel, grid, dim3(kThreads), 0, s, table, (int32_t)N, (int32_t)K, ids, units,
+                           runs, out);
     return hipGetLastError();
 }
 

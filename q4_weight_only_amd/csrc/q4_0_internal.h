@@ -56,6 +56,8 @@ hipError_t launch_unpack(const uint8_t *packed, int64_t N, int64_t K, uint8_t *g
 hipError_t launch_dequant(const uint8_t *packed, int64_t N, int64_t K, float *w, hipStream_t s);
 hipError_t launch_embed(const uint8_t *packed, int64_t N, int64_t K, const int32_t *ids, int64_t n_ids,
                         float *out, hipStream_t s);
+hipError_t launch_embed_gguf(const uint8_t *gguf, int64_t N, int64_t K, const int32_t *ids, int64_t n_ids,
+                             float *out, hipStream_t s);
 
 // Runs the fused linear over all segments of `a` (segments' tile_begin is
 // filled in by the launcher).

@@ -160,8 +160,9 @@ def test_linear_kernel_names(L):
     assert kn(300, 3072, arr(3072), 1) == b"gemm3_kernel<4, 1, 1, 8, 4, 8, false>"
 
 
-def test_embed_validates_first(L):
-    em = L.q4_0_embed
+@pytest.mark.parametrize("fn", ["q4_0_embed", "q4_0_embed_gguf"])
+def test_embed_validates_first(L, fn):
+    em = getattr(L, fn)
     assert em(FAKE, 16, 48, FAKE, 4, FAKE, None) == SHAPE          # K % 32
     assert em(FAKE, 0, 64, FAKE, 4, FAKE, None) == SHAPE           # N < 1
     assert em(FAKE, 16, 64, FAKE, -1, FAKE, None) == SHAPE         # n_ids < 0
