@@ -264,7 +264,7 @@ def time_swiglu(prepared, ms, reps, dev):
                         q4.linear_swiglu(x, pws[0], pws[1], h16, dtype=torch.bfloat16)
                     else:
                         q4.linear_multi(x, pws, ys)
-                    if r > 0:              # the first round warms up
+                    if r > 0:              # the first pass warms up
                         pairs[kind].append((a, b))
         torch.cuda.synchronize(dev)
         t = {kind: float(np.mean([a.elapsed_time(b) / 1e3 for a, b in v])) for kind, v in pairs.items()}
