@@ -27,7 +27,7 @@ def _run_and_check(w32, x_bits, what):
 
 
 MS = [1, 2, 3, 4, 5, 16, 17, 31, 32, 33, 64, 100, 129, 300, 2100]
-NKS = [(16, 32), (48, 128), (40, 96), (200, 384), (1040, 1280), (96, 3072)]
+NKS = [(16, 32), (48, 128), (40, 96), (200, 384), (1040, 1280), (96, 3072), (72, 3104)]
 
 
 @pytest.mark.parametrize("m", MS)
