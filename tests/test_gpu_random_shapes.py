@@ -1,6 +1,6 @@
 """Seeded random launches across the dispatch table: M from 1 to 300 (and a
 few tall one-row launches that take the stream kernel), 1-4 segments of
-ragged N, K any multiple of 32.  Every output element against the oracle's
+ragged N, K any multiple of 32 up to 5120.  Every output element against the oracle's
 bound; each case prints its shape and kernel first."""
 
 import numpy as np
@@ -25,7 +25,7 @@ def _case(seed):
         ns = [int(rng.integers(2048 * 16, 2400 * 16))]
         return m, k, ns
     m = int(rng.choice([1, 2, 3, 4, 5, 8, 16, 17, 24, 32, 33, 48, 64, 65, 100, 129, 200, 300]))
-    k = 32 * int(rng.integers(1, 97))
+    k = 32 * int(rng.integers(1, 161))
     nseg = int(rng.integers(1, 5))
     ns = [int(rng.integers(1, 1600)) for _ in range(nseg)]
     while m * sum(ns) * k > BUDGET:
