@@ -36,6 +36,8 @@ COMMON_FLAGS = [
     # MFMA results in VGPRs: the per-block fp32 rescale reads them directly
     # instead of copying each one out of an AGPR first.
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    "-Wall",
+    "-Wextra",
     "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
@@ -71,10 +73,11 @@ def build(verbose: bool = False) -> str:
         cmds.append([hipcc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         outs = list(ex.map(_run, cmds))
-    if verbose:
-        for o in outs:
-            if o.strip():
-                print(o)
+    for o in outs:
+        # compiler warnings are always shown; other output only when asked
+        shown = o if verbose else "\n".join(l for l in o.splitlines() if "warning:" in l)
+        if shown.strip():
+            print(shown)
     tmp = LIB + f".tmp{os.getpid()}"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
