@@ -803,12 +803,14 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[MT - 1][nt][r] = fmaf(d, D[MT - 1][r], acc[MT - 1][nt][r]);
         }
-        // blocks in pairs: within a pair the compiler may pull the second
-        // block's x reads up among the first block's MFMAs (hiding their LDS
-        // latency); the barrier between pairs bounds the live MFMA results
-        // and operands.  Against a barrier after every block: +3-4% at
-        // M = 2048, +5-6% at M = 1505 (113 VGPRs either way).
-        if (i & 1) __builtin_amdgcn_sched_barrier(0);
+        // blocks in groups: within a group the compiler may pull a block's x
+        // reads up among the previous block's MFMAs (hiding their LDS
+        // latency); the barrier between groups bounds the live MFMA results
+        // and operands.  Groups of 2 blocks for 8 m-tiles, of 4 (a whole
+        // step) for 4 m-tiles.  Against a barrier after every block: +3-4%
+        // at M = 2048 and +5-6% at M = 1505 (128-row tiles, 113 VGPRs either
+        // way), +3-9% at M = 130 and 300 (64-row tiles).
+        if ((i + 1) % (MT >= 8 ? 2 : 4) == 0) __builtin_amdgcn_sched_barrier(0);
     };
 
     u32x4 R0[NPT], R1[NPT];
