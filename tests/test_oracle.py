@@ -215,6 +215,51 @@ def test_output_row_follows_weight_row_not_activation_row():
     assert np.array_equal(y, np.array([[0.0, 32.0, 0.0], [0.0, 64.0, 0.0]]))
 
 
+def _bound_blocks():
+    """Two one-block rows built by hand, and two rows of x.
+
+    W row 0: d = 0.5,   q_j = j % 16      -> w_0j = (j % 16 - 8) / 2
+    W row 1: d = -0.25, q_j = 15 - j % 16 -> w_1j = (7 - j % 16) * -1/4
+    x row 0: x_0j = (-1)^j (j + 1) / 4   (0.25, -0.5, ..., -8: bf16-exact)
+    x row 1: x_1j = 1 for j < 16, -2 for j >= 16
+    """
+    k = 32
+    rows = [_block(0.5, [j % 16 for j in range(k)]), _block(-0.25, [15 - j % 16 for j in range(k)])]
+    blocks = np.stack(rows).reshape(2, 1, 18)
+    x = np.array([[(-1) ** j * (j + 1) / 4 for j in range(k)],
+                  [1.0 if j < 16 else -2.0 for j in range(k)]], dtype=np.float32)
+    return inputs.bf16_bits_from_f32(x), blocks
+
+
+def test_error_bound_by_hand():
+    """1e-3 * sum_k |x_k w_k| + 1e-6 on hand-built blocks, worked on paper.
+
+    With a_i = |i - 8| = 8,7,...,1,0,1,...,7 and b_i = |7 - i| = 7,...,1,0,1,...,8
+    (i = 0..15; sum a = sum b = 64, sum (i+1) a_i = 512, sum (i+1) b_i = 576):
+      sum |x_0 w_0| = 1/8  * (512 + (16*64 + 512))   = 256
+      sum |x_0 w_1| = 1/16 * (576 + (16*64 + 576))   = 136
+      sum |x_1 w_0| = 1/2 * 64 + 2 * 1/2 * 64       = 96
+      sum |x_1 w_1| = 1/4 * 64 + 2 * 1/4 * 64       = 48
+    The signed sums are -32, -17, 4, -2, and |x| against the signed w gives
+    52, 59, -12, 6, so a bound built on either is caught here.
+    """
+    x_bits, blocks = _bound_blocks()
+    got = O.error_bound(x_bits, blocks, 2, 32)
+    want = np.array([[0.256001, 0.136001], [0.096001, 0.048001]])
+    assert got.shape == (2, 2)
+    assert np.allclose(got, want, rtol=1e-12, atol=0)
+
+
+def test_error_bound_uses_each_blocks_own_scale():
+    """One row of two blocks: w = +1 (d = 1, q = 9) on block 0 and
+    w = (6 - 8) * -3 = +6 on block 1; x = 1 on block 0, 0.5 on block 1:
+    sum |x w| = 32 * 1 + 32 * 0.5 * 6 = 128."""
+    blocks = np.concatenate([_block(1.0, [9] * 32), _block(-3.0, [6] * 32)]).reshape(1, 2, 18)
+    x_bits = inputs.bf16_bits_from_f32(np.array([[1.0] * 32 + [0.5] * 32], dtype=np.float32))
+    assert O.error_bound(x_bits, blocks, 1, 64)[0, 0] == pytest.approx(0.128001, rel=1e-12)
+    assert O.linear(x_bits, blocks, 1, 64)[0, 0] == 128.0
+
+
 def test_linear_rows_matches_full_linear():
     rng = np.random.default_rng(6)
     n, k = 40, 256
@@ -398,6 +443,37 @@ def test_planted_mistakes_are_caught(monkeypatch):
                 except AssertionError:
                     failed += 1
             assert failed > 0, name
+
+
+_ORIG_BOUND = O.error_bound
+
+
+def _bound_mutant(kind):
+    def fn(x_bits, blocks, n, k, chunk_rows=8192):
+        x = O.bf16_bits_to_f64(x_bits).reshape(-1, k)
+        w = _ORIG_DEQUANT(blocks, n, k).astype(np.float64)
+        if kind == "factor 1e-2":
+            return 1e-2 * (np.abs(x) @ np.abs(w).T) + 1e-6
+        if kind == "signed sum":
+            return 1e-3 * (x @ w.T) + 1e-6
+        return 1e-3 * (np.abs(x) @ w.T) + 1e-6          # |x| without |w|
+    return fn
+
+
+def test_planted_error_bound_mistakes_are_caught(monkeypatch):
+    """A wrong factor, the signed sum x w^T, or |x| against the signed w must
+    each fail the hand-worked bound pins."""
+    for kind in ("factor 1e-2", "signed sum", "abs x only"):
+        with monkeypatch.context() as mp:
+            mp.setattr(O, "error_bound", _bound_mutant(kind))
+            failed = 0
+            for chk in (test_error_bound_by_hand, test_error_bound_uses_each_blocks_own_scale):
+                try:
+                    chk()
+                except AssertionError:
+                    failed += 1
+            assert failed > 0, kind
+    assert O.error_bound is _ORIG_BOUND
 
 
 def test_planted_quantizer_mistakes_are_caught():

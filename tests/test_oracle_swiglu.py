@@ -135,6 +135,34 @@ def test_swiglu_bound_covers_perturbations():
     assert worst > 0.3          # not vacuous
 
 
+def test_swiglu_bound_by_hand():
+    """Two outputs, K = 32, d = 1, x = (2, 1, 0, ..., 0), worked on paper:
+
+    column 0: gate w = (+1, -2) -> g = 0, sum|x w| = 4 -> bg = 0.004001;
+              up w_0 = +3      -> u = 6, sum|x w| = 6 -> bu = 0.006001;
+              silu(0) = 0, so the bound is 1.1 * bg * (|u| + bu).
+    column 1: gate w_0 = +1 -> g = 2, bg = 0.002001;
+              up w_1 = +2   -> u = 2, bu = 0.002001;
+              bound 1.1 bg (|u| + bu) + silu(2) bu + 1e-5 |silu(2) u|.
+    """
+    k, n = 32, 2
+    qg0, qu0, qg1, qu1 = [8] * 32, [8] * 32, [8] * 32, [8] * 32
+    qg0[0], qg0[1], qu0[0] = 9, 6, 11
+    qg1[0], qu1[1] = 9, 10
+    gate = np.stack([_block(1.0, qg0), _block(1.0, qg1)]).reshape(n, 1, 18)
+    up = np.stack([_block(1.0, qu0), _block(1.0, qu1)]).reshape(n, 1, 18)
+    x = np.zeros(k, dtype=np.float32)
+    x[0], x[1] = 2.0, 1.0
+    xb = _bf16_bits(x)[None, :]
+    s2 = 2.0 / (1.0 + math.exp(-2.0))
+    want = [1.1 * 0.004001 * (6 + 0.006001),
+            1.1 * 0.002001 * (2 + 0.002001) + s2 * 0.002001 + 1e-5 * s2 * 2]
+    got = O.swiglu_bound(xb, gate, up, n, k)
+    assert got.shape == (1, 2)
+    assert got[0].tolist() == pytest.approx(want, rel=1e-12)
+    assert want[0] == pytest.approx(0.0264330110011, rel=1e-12)
+
+
 def test_planted_sign_slip_is_caught(monkeypatch):
     orig = O.silu
 
@@ -146,3 +174,12 @@ def test_planted_sign_slip_is_caught(monkeypatch):
         test_silu_closed_forms()
     with pytest.raises(AssertionError):
         test_swiglu_hand_values_and_asymmetry()
+
+
+def test_swiglu_bound_catches_a_wrong_linear_bound(monkeypatch):
+    """swiglu_bound is built on error_bound; a tenfold error_bound must fail
+    the hand-worked SwiGLU bound as well."""
+    orig = O.error_bound
+    monkeypatch.setattr(O, "error_bound", lambda *a, **kw: 10.0 * orig(*a, **kw))
+    with pytest.raises(AssertionError):
+        test_swiglu_bound_by_hand()
