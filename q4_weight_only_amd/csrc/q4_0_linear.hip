@@ -35,6 +35,8 @@
 // No kernel uses atomics: results are bitwise reproducible.
 
 #include <atomic>
+#include <string>
+#include <vector>
 
 #include <hip/hip_ext.h>
 #include <hip/hip_bf16.h>
@@ -338,6 +340,182 @@ void skinny_kernel(const LinearArgs a) {
     }
 }
 
+// ------------------------------------------------------------------- gemv
+// Word 3 of a raw buffer resource on gfx9: 32-bit data format, so untyped
+// loads are bounds-checked against the resource's byte size and read zero
+// past it.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kOutOfRange = 0x40000000;   // a byte offset beyond every x resource (at most 2^29 bytes)
+constexpr int kNonTemporal = 2;           // cache-policy bit of a buffer load: streaming (nt)
+
+// Decode batches (up to 16 rows, short K): skinny_kernel<MROWS, 1, WK, P>'s
+// work split and arithmetic -- wave wk owns super-tiles wk, wk + WK, ... of
+// one 16-row weight tile, blocks are added in k order and the WK partial sums
+// through LDS in wave order, so both give the same bits -- with a different
+// issue order.  The x loads go out first, then every one of the wave's NS
+// weight stages (NS = ceil(KT / WK), fixed at compile time, so the code is
+// straight-line and each wait names an exact count).  Loads complete in issue
+// order for the wait counter: the x store to LDS waits for x alone, and the
+// MFMAs of stage j wait for stage j alone, so blocks are decoded and
+// multiplied while the later stages are still arriving.  A stage past the
+// last super-tile (when WK does not divide KT) reads the last tile with its
+// scales forced to zero, which adds nothing (and x is read from that tile's
+// columns, zero past K).  Weights are read through buffer resources, whose
+// base and size sit in scalar registers, at one per-lane offset.
+//
+// GLU: the launch has two segments of the same shape, gate (seg 0, whose y
+// receives the result) and up (seg 1).  Workgroup 2 rt + h covers the eight
+// rows 16 rt + 8 h .. + 7 of both: MFMA columns 0-7 are those gate rows and
+// columns 8-15 the same up rows (each lane reads its 16 bytes from the gate
+// or the up tile), so a gated launch has the plain launch's workgroups,
+// waves and bytes per wave.  A column's result does not depend on its
+// neighbours, so g and u are the plain launch's values; after the reduction
+// lane c < 8 takes u from lane c + 8 and stores silu(g) * u.
+template <int MROWS, int WK, int NS, int WPE, bool GLU>
+__global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
+void gemv_kernel(const LinearArgs a) {
+    static_assert(MROWS >= 1 && MROWS <= 16, "one 16-row m-tile");
+    constexpr int REGS = MROWS < 4 ? MROWS : 4;
+    constexpr int kThreads = 64 * WK;
+    extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+    const int lane = threadIdx.x & 63;
+    const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nl = lane & 15, g = lane >> 4;
+
+    const int s = GLU ? 0 : find_segment(a, blockIdx.x);
+    const Segment sg = a.seg[s];
+    // plain: 16-row tile rt0; gated: tile rt0, rows 8 h .. 8 h + 7 of it
+    const int rt0 = GLU ? static_cast<int>(blockIdx.x) >> 1 : static_cast<int>(blockIdx.x) - sg.tile_begin;
+    const int half = GLU ? static_cast<int>(blockIdx.x) & 1 : 0;
+    const int KT = a.KT;
+    const int mrows = a.M < MROWS ? a.M : MROWS;
+    const int row_bytes = x_row_bytes(KT);
+
+    // x chunks (16 bytes) of the staged tile: KT <= NS * WK super-tiles of
+    // 16 chunks per row, so a thread owns at most kXPer of them
+    constexpr int kXPer = (MROWS * NS * WK * (kTileK / 8) + kThreads - 1) / kThreads;
+    const int chunks_per_row = KT * (kTileK / 8);
+    const int xtotal = mrows * chunks_per_row;
+
+    // weights: past the segment's end the last tile is read (its outputs are
+    // never stored)
+    const int rt = rt0 < sg.RT ? rt0 : sg.RT - 1;
+    const int64_t T0 = static_cast<int64_t>(rt) * KT;
+    __amdgpu_buffer_rsrc_t nib_rsrc, sc_rsrc;
+    const uint8_t *nib_lane = nullptr;
+    const uint8_t *sc_lane = nullptr;
+    if constexpr (GLU) {
+        // row r of the tile for this lane's column: gate rows in columns 0-7,
+        // the same up rows in columns 8-15
+        const Segment &src = a.seg[nl < 8 ? 0 : 1];
+        const int r = 8 * half + (nl & 7);
+        nib_lane = src.nib + T0 * kTileNibBytes + g * 256 + r * 16;
+        sc_lane = reinterpret_cast<const uint8_t *>(src.scales + T0 * kTileScales + r * 4);
+    } else {
+        nib_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(sg.nib + T0 * kTileNibBytes), 0,
+                                                     KT * kTileNibBytes, kBufferRsrcWord3);
+        sc_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(sg.scales + T0 * kTileScales), 0,
+                                                    KT * kTileScales * 2, kBufferRsrcWord3);
+    }
+
+    // 1. x first: every chunk of this thread, zero past K (a chunk past the
+    //    row's K, or a thread without a chunk, reads beyond the resource)
+    const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.x), 0, mrows * a.K * 2, kBufferRsrcWord3);
+    u32x4 xv[kXPer];
+    int xdst[kXPer];
+#pragma unroll
+    for (int q = 0; q < kXPer; ++q) {
+        const int c = threadIdx.x + q * kThreads;
+        const int m = c / chunks_per_row, kc = c - m * chunks_per_row;
+        const bool in = c < xtotal && kc * 8 < a.K;
+        // a thread without a chunk stores its zeros to the pad slot after the tile
+        xdst[q] = c < xtotal ? m * row_bytes + kc * 16 : mrows * row_bytes;
+        xv[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              xrsrc, in ? (m * a.K + kc * 8) * 2 : kOutOfRange, 0, 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep the x loads ahead of the weights
+
+    // 2. then every weight stage of this wave, each one's codes then scales
+    u32x4 nib[NS];
+    u32x2 sc[NS];
+    int ktj[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int kt = wk + j * WK;
+        ktj[j] = kt < KT ? kt : KT - 1;
+        if constexpr (GLU) {
+            nib[j] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(nib_lane + static_cast<int64_t>(ktj[j]) * kTileNibBytes));
+            sc[j] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x2 *>(sc_lane + static_cast<int64_t>(ktj[j]) * kTileScales * 2));
+        } else {
+            nib[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   nib_rsrc, lane * 16, ktj[j] * kTileNibBytes, kNonTemporal));
+            sc[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                  sc_rsrc, nl * 8, ktj[j] * kTileScales * 2, kNonTemporal));
+        }
+        __builtin_amdgcn_sched_barrier(0);   // stages go out in order
+    }
+    // 3. x into LDS (waits for the x loads only), one barrier
+#pragma unroll
+    for (int q = 0; q < kXPer; ++q) *reinterpret_cast<u32x4 *>(xs + xdst[q]) = xv[q];
+    __syncthreads();
+
+    // 4. stage j's MFMAs wait for stage j's weights only
+    const int a_off = (nl < mrows ? nl : mrows - 1) * row_bytes + g * 16;
+    floatx4 acc = (floatx4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const bool live = wk + j * WK < KT;
+#pragma unroll
+        for (int i = 0; i < kTileBlocks; ++i) {
+            const int b = ktj[j] * kTileBlocks + i;
+            const bf16x8 A = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xs + a_off + b * kQK * 2));
+            const bf16x8 B = decode_piece(piece_of(nib[j], i));
+            const float d = live ? scale_of(sc[j], i) : 0.0f;
+            const floatx4 D = mfma_block(A, B);
+#pragma unroll
+            for (int r = 0; r < REGS; ++r) acc[r] = fmaf(d, D[r], acc[r]);
+        }
+    }
+
+    // wave-ordered sum of the K slices
+    if constexpr (WK > 1) {
+        __shared__ float red[WK - 1][REGS][64];
+        if (wk > 0) {
+#pragma unroll
+            for (int r = 0; r < REGS; ++r) red[wk - 1][r][lane] = acc[r];
+        }
+        __syncthreads();
+        if (wk != 0) return;
+#pragma unroll
+        for (int w = 0; w < WK - 1; ++w)
+#pragma unroll
+            for (int r = 0; r < REGS; ++r) acc[r] += red[w][r][lane];
+    }
+    if constexpr (GLU) {
+        float u[REGS];
+#pragma unroll
+        for (int r = 0; r < REGS; ++r) u[r] = __shfl_xor(acc[r], 8, 64);   // column c + 8: the up row of c
+        const int n = rt0 * 16 + 8 * half + nl;
+        if (nl >= 8 || rt0 >= sg.RT || n >= sg.N) return;
+#pragma unroll
+        for (int r = 0; r < REGS; ++r) {
+            const int m = 4 * g + r;
+            if (m < a.M) store_out(a, sg, static_cast<int64_t>(m) * sg.N + n, silu_f32(acc[r] * 16.0f) * (u[r] * 16.0f));
+        }
+    } else {
+        const int n = rt0 * 16 + nl;
+        if (rt0 >= sg.RT || n >= sg.N) return;
+#pragma unroll
+        for (int r = 0; r < REGS; ++r) {
+            const int m = 4 * g + r;
+            if (m < a.M) sg.y[static_cast<int64_t>(m) * sg.N + n] = acc[r] * 16.0f;
+        }
+    }
+}
+
 // ----------------------------------------------------------- skinny stream
 // Very tall weights (the LM head: thousands of 16-row tiles in one launch).
 // A grid of as many workgroups as the device holds at once, each walking the
@@ -481,12 +659,6 @@ struct GemmCfg {
 // chunk index is XORed with the row's low 4 bits, so the 16 rows read by one
 // MFMA A fragment (same chunk) land in 16 different chunk slots.
 __device__ __forceinline__ int a_tile_offset(int m, int c) { return (m * 16 + (c ^ (m & 15))) * 16; }
-
-// Word 3 of a raw buffer resource on gfx9: 32-bit data format, so untyped
-// loads are bounds-checked against the resource's byte size and read zero
-// past it.
-constexpr int kBufferRsrcWord3 = 0x00020000;
-constexpr int kOutOfRange = 0x40000000;   // a byte offset beyond every x resource (at most 2^29 bytes)
 
 // PB weight stages per wave: the loads for step kt + PB - 1 are issued while
 // step kt computes (the x tile is double-buffered in LDS either way).  Each
@@ -648,6 +820,9 @@ void gemm_kernel(const LinearArgs a) {
 }
 
 // ------------------------------------------------------------------- gemm3
+#ifndef GEMM_BATCH
+#define GEMM_BATCH 1
+#endif
 // Prefill-sized M with register tiles of MT x NT MFMA tiles per wave.  The
 // x tile of the next 128-k step is staged a quarter per block step (so the
 // staging registers stay few) into the other LDS buffer; the rescale of
@@ -790,6 +965,21 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
         for (int nt = 0; nt < NT; ++nt) {
             const bf16x8 B = decode_piece(piece_of(S.nib[nt], i));
             const float d = scale_of(S.sc[nt], i);
+#if GEMM_BATCH > 1
+            constexpr int BT = GEMM_BATCH < MT ? GEMM_BATCH : MT;
+#pragma unroll
+            for (int mb = 0; mb < MT; mb += BT) {
+                floatx4 D[BT];
+#pragma unroll
+                for (int u = 0; u < BT; ++u) D[u] = mfma_block(A[mb + u], B);
+                __builtin_amdgcn_sched_group_barrier(0x008, BT, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4 * BT, 0);
+#pragma unroll
+                for (int u = 0; u < BT; ++u)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[mb + u][nt][r] = fmaf(d, D[u][r], acc[mb + u][nt][r]);
+            }
+#else
             // each MFMA's rescale is issued after the next MFMA, so the FMAs
             // never wait on a result still in the matrix pipe
             floatx4 D[MT];
@@ -802,6 +992,7 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[MT - 1][nt][r] = fmaf(d, D[MT - 1][r], acc[MT - 1][nt][r]);
+#endif
         }
         // blocks in groups: within a group the compiler may pull a block's x
         // reads up among the previous block's MFMAs (hiding their LDS
@@ -1037,6 +1228,41 @@ hipError_t run_skinny(LinearArgs a, hipStream_t s) {
     return launch_kernel(skinny_kernel<MROWS, NT, WK, P, false, WPE, GLU>, dim3(tiles), dim3(kThreads), 0, s, a);
 }
 
+// The decode kernel with x staged in LDS and all NS = ceil(KT / WK) weight
+// stages of a wave in flight at once: up to kGemvMaxStages stages.  The
+// dispatch takes it for M <= 4 and K <= 4096 only, where x takes at most
+// 4 rows of 8 KiB of LDS; the launcher instantiates one kernel per NS.
+constexpr int kGemvMaxStages = 6;
+inline int gemv_stages(const LinearArgs &a, int wk) { return (a.KT + wk - 1) / wk; }
+
+template <int MROWS, int WK, int NS, int WPE, bool GLU>
+hipError_t launch_gemv_ns(const LinearArgs &a, int tiles, uint32_t lds, hipStream_t s) {
+    auto kernel = gemv_kernel<MROWS, WK, NS, WPE, GLU>;
+    static std::atomic<uint64_t> lds_allowed{0};
+    const hipError_t e = allow_dynamic_lds(kernel, lds_allowed);
+    if (e != hipSuccess) return e;
+    return launch_kernel(kernel, dim3(tiles), dim3(64 * WK), lds, s, a);
+}
+
+// NSMAX: the most stages the dispatch can ask of this configuration (only
+// those stage counts are instantiated).
+template <int MROWS, int WK, int WPE, bool GLU, int NSMAX>
+hipError_t run_gemv(LinearArgs a, hipStream_t s) {
+    static_assert(NSMAX >= 1 && NSMAX <= kGemvMaxStages, "stage count");
+    const int tiles = assign_tiles<GLU>(a, 1) * (GLU ? 2 : 1);   // gated: two 8-row halves per tile
+    const uint32_t lds = static_cast<uint32_t>(skinny_x_bytes(a.M, a.K, MROWS)) + 16;   // + the pad slot
+    switch (gemv_stages(a, WK)) {
+        case 1: return launch_gemv_ns<MROWS, WK, 1, WPE, GLU>(a, tiles, lds, s);
+        case 2: if constexpr (NSMAX >= 2) return launch_gemv_ns<MROWS, WK, 2, WPE, GLU>(a, tiles, lds, s); break;
+        case 3: if constexpr (NSMAX >= 3) return launch_gemv_ns<MROWS, WK, 3, WPE, GLU>(a, tiles, lds, s); break;
+        case 4: if constexpr (NSMAX >= 4) return launch_gemv_ns<MROWS, WK, 4, WPE, GLU>(a, tiles, lds, s); break;
+        case 5: if constexpr (NSMAX >= 5) return launch_gemv_ns<MROWS, WK, 5, WPE, GLU>(a, tiles, lds, s); break;
+        case 6: if constexpr (NSMAX >= 6) return launch_gemv_ns<MROWS, WK, 6, WPE, GLU>(a, tiles, lds, s); break;
+        default: break;
+    }
+    return hipErrorInvalidValue;   // the dispatch never asks for more than NSMAX stages
+}
+
 template <int MT, int NT, int WM, int WN, int WPE = 0, int PB = 2>
 hipError_t run_gemm(LinearArgs a, hipStream_t s) {
     using C = GemmCfg<MT, NT, WM, WN>;
@@ -1099,16 +1325,27 @@ bool take_launch_events(hipEvent_t &start, hipEvent_t &stop) {
 // results of an output in the same order, so the choice never changes a
 // result.
 namespace {
-enum class Cfg { M1, M1Stream, M1Long, M2, M2Long, M4, M4Long, M16, M16Long, M32, M32Split, M32Split2, M64, M64Split,
+enum class Cfg { G1, G1K, G2, G2K, G4, G4K, M1Stream, M1Long, M2Long, M4Long, M16, M16Long, M32, M32Split, M32Split2,
+                 M64, M64Split,
                  Gemm64, Gemm128, Gemm128W };
 
 // Configuration by M and K alone: the decode sizes, and the gated launch's
 // GEMM split at 2048 rows.
 Cfg pick_mk(int64_t M, int64_t K) {
+    // up to 4 rows: the decode kernel with every stage in flight for K up to
+    // 4096 (3 or 4 stages per wave); longer rows keep the 2-stage refill of
+    // the K-split kernel, which measured faster there (down 9216 -> 3072:
+    // 7.6 against 8.2 us with five stages in flight)
+    if (M <= 4 && K <= 4096) {
+        const bool k3 = K <= 3072;
+        if (M == 1) return k3 ? Cfg::G1 : Cfg::G1K;
+        if (M == 2) return k3 ? Cfg::G2 : Cfg::G2K;
+        return k3 ? Cfg::G4 : Cfg::G4K;
+    }
+    if (M == 1) return Cfg::M1Long;
+    if (M == 2) return Cfg::M2Long;
+    if (M <= 4) return Cfg::M4Long;
     const bool long_k = K > 3072;
-    if (M == 1) return long_k ? Cfg::M1Long : Cfg::M1;
-    if (M == 2) return long_k ? Cfg::M2Long : Cfg::M2;
-    if (M <= 4) return long_k ? Cfg::M4Long : Cfg::M4;
     if (M <= 16) return long_k ? Cfg::M16Long : Cfg::M16;
     if (M <= 32) return Cfg::M32;
     if (M <= 64) return Cfg::M64;
@@ -1153,7 +1390,7 @@ Cfg pick(const LinearArgs &a) {
     if (a.M <= 64) {
         const Cfg c = pick_mk(a.M, a.K);
         if (c == Cfg::M32 || c == Cfg::M64) return pick_17_64(a, c);
-        return c == Cfg::M1 && stream_m1(a) ? Cfg::M1Stream : c;
+        return c == Cfg::G1 && stream_m1(a) ? Cfg::M1Stream : c;
     }
     const int64_t cus = device_cus();
     auto cost = [&](int bm, int bn, int64_t unit) { return (gemm_tiles(a, bm, bn) + cus - 1) / cus * unit; };
@@ -1168,15 +1405,55 @@ const char *skinny_name(int64_t M, int64_t K, int mrows_max, const char *lds_nam
 }
 }  // namespace
 
+// Name of a gemv_kernel instantiation (static string): the stage count
+// follows from K, so the names come from a table built once.
+const char *gemv_name(int mrows, int wk, int ns, int wpe, bool glu) {
+    static const std::vector<std::string> table = [] {
+        std::vector<std::string> t;
+        for (int m : {1, 2, 4})
+            for (int w : {4, 8, 16})
+                for (int n = 1; n <= kGemvMaxStages; ++n)
+                    for (int e : {0, 6})
+                        for (int gl : {0, 1})
+                            t.push_back("gemv_kernel<" + std::to_string(m) + ", " + std::to_string(w) + ", " +
+                                        std::to_string(n) + ", " + std::to_string(e) + ", " +
+                                        (gl ? "true" : "false") + ">");
+        return t;
+    }();
+    const int mi = mrows == 1 ? 0 : mrows == 2 ? 1 : 2, wi = wk == 4 ? 0 : wk == 8 ? 1 : 2;
+    if (ns < 1 || ns > kGemvMaxStages) return "";
+    return table[((((mi * 3 + wi) * kGemvMaxStages + ns - 1) * 2 + (wpe ? 1 : 0)) * 2 + (glu ? 1 : 0))].c_str();
+}
+
+// The decode configurations: rows, K-slices and waves-per-EU hint by M and K.
+struct GemvCfg {
+    int mrows, wk, wpe;
+};
+GemvCfg gemv_cfg(Cfg c) {
+    switch (c) {
+        case Cfg::G1: return {1, 8, 6};
+        case Cfg::G1K: return {1, 16, 0};
+        case Cfg::G2: return {2, 4, 0};
+        case Cfg::G2K: return {2, 8, 0};
+        case Cfg::G4: return {4, 8, 0};
+        default: return {4, 16, 0};   // G4K
+    }
+}
+bool is_gemv(Cfg c) {
+    return c == Cfg::G1 || c == Cfg::G1K || c == Cfg::G2 || c == Cfg::G2K || c == Cfg::G4 || c == Cfg::G4K;
+}
+
 const char *linear_config_name(const LinearArgs &a) {
     const int64_t M = a.M, K = a.K;
-    switch (pick(a)) {
-        case Cfg::M1: return skinny_name(M, K, 1, "skinny_kernel<1, 1, 8, 3, true, 6, false>", "skinny_kernel<1, 1, 8, 3, false, 6, false>");
+    const Cfg c = pick(a);
+    if (is_gemv(c)) {
+        const GemvCfg g = gemv_cfg(c);
+        return gemv_name(g.mrows, g.wk, gemv_stages(a, g.wk), g.wpe, false);
+    }
+    switch (c) {
         case Cfg::M1Stream: return "skinny_stream_kernel<1, 8, 3, 6>";
         case Cfg::M1Long: return skinny_name(M, K, 1, "skinny_kernel<1, 1, 16, 2, true, 0, false>", "skinny_kernel<1, 1, 16, 2, false, 0, false>");
-        case Cfg::M2: return skinny_name(M, K, 2, "skinny_kernel<2, 1, 4, 2, true, 6, false>", "skinny_kernel<2, 1, 4, 2, false, 6, false>");
         case Cfg::M2Long: return skinny_name(M, K, 2, "skinny_kernel<2, 1, 16, 2, true, 0, false>", "skinny_kernel<2, 1, 16, 2, false, 0, false>");
-        case Cfg::M4: return skinny_name(M, K, 4, "skinny_kernel<4, 1, 4, 2, true, 0, false>", "skinny_kernel<4, 1, 4, 2, false, 0, false>");
         case Cfg::M4Long: return skinny_name(M, K, 4, "skinny_kernel<4, 1, 16, 2, true, 0, false>", "skinny_kernel<4, 1, 16, 2, false, 0, false>");
         case Cfg::M16: return skinny_name(M, K, 16, "skinny_kernel<16, 1, 4, 2, true, 0, false>", "skinny_kernel<16, 1, 4, 2, false, 0, false>");
         case Cfg::M16Long: return skinny_name(M, K, 16, "skinny_kernel<16, 1, 16, 2, true, 0, false>", "skinny_kernel<16, 1, 16, 2, false, 0, false>");
@@ -1193,13 +1470,16 @@ const char *linear_config_name(const LinearArgs &a) {
 
 hipError_t launch_linear(LinearArgs a, hipStream_t s) {
     switch (pick(a)) {
-        case Cfg::M1: return run_skinny<1, 1, 8, 3, 6>(a, s);
-        case Cfg::M1Stream: return run_skinny_stream<1, 8, 3, 6>(a, s);
+        case Cfg::G1: return run_gemv<1, 8, 6, false, 3>(a, s);
+        case Cfg::G1K: return run_gemv<1, 16, 0, false, 2>(a, s);
+        case Cfg::G2: return run_gemv<2, 4, 0, false, 6>(a, s);
+        case Cfg::G2K: return run_gemv<2, 8, 0, false, 4>(a, s);
+        case Cfg::G4: return run_gemv<4, 8, 0, false, 3>(a, s);
+        case Cfg::G4K: return run_gemv<4, 16, 0, false, 2>(a, s);
         case Cfg::M1Long: return run_skinny<1, 1, 16, 2, 0>(a, s);
-        case Cfg::M2: return run_skinny<2, 1, 4, 2, 6>(a, s);
         case Cfg::M2Long: return run_skinny<2, 1, 16, 2, 0>(a, s);
-        case Cfg::M4: return run_skinny<4, 1, 4, 2, 0>(a, s);
         case Cfg::M4Long: return run_skinny<4, 1, 16, 2, 0>(a, s);
+        case Cfg::M1Stream: return run_skinny_stream<1, 8, 3, 6>(a, s);
         case Cfg::M16: return run_skinny<16, 1, 4, 2, 0>(a, s);
         case Cfg::M16Long: return run_skinny<16, 1, 16, 2, 0>(a, s);
         case Cfg::M32: return run_gemm<2, 1, 1, 8, 0, 2>(a, s);
@@ -1209,7 +1489,11 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
         case Cfg::M64Split: return run_skinny<64, 1, 8, 2, 0>(a, s);
         case Cfg::Gemm64: return run_gemm3<4, 1, 1, 8, 4, 8>(a, s);
         case Cfg::Gemm128W: return run_gemm3<8, 1, 1, 12, 0, 8>(a, s);
+#ifdef GEMM128_CFG
+        default: return run_gemm3<GEMM128_CFG>(a, s);
+#else
         default: return run_gemm3<8, 1, 1, 8, 4, 8>(a, s);
+#endif
     }
 }
 
@@ -1217,13 +1501,19 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
 // rows of a tile on separate waves (skinny: 2 WK waves, at most 8 K-slices
 // so a workgroup stays within 1024 threads; gemm3: WN / 2 gate and WN / 2 up
 // waves), so every wave runs the plain arithmetic.
+// The gated launch's decode configurations are the plain ones (its
+// workgroups cover 8 gate and 8 up rows: the plain wave count per workgroup).
+GemvCfg gemv_glu_cfg(Cfg c) { return gemv_cfg(c); }
+
 const char *linear_glu_config_name(int64_t M, int64_t K) {
-    switch (pick_mk(M, K)) {
-        case Cfg::M1: return skinny_name(M, K, 1, "skinny_kernel<1, 1, 4, 2, true, 6, true>", "skinny_kernel<1, 1, 4, 2, false, 6, true>");
+    const Cfg c = pick_mk(M, K);
+    if (is_gemv(c)) {
+        const GemvCfg g = gemv_glu_cfg(c);
+        return gemv_name(g.mrows, g.wk, static_cast<int>((round_up(K, kTileK) / kTileK + g.wk - 1) / g.wk), g.wpe, true);
+    }
+    switch (c) {
         case Cfg::M1Long: return skinny_name(M, K, 1, "skinny_kernel<1, 1, 8, 3, true, 0, true>", "skinny_kernel<1, 1, 8, 3, false, 0, true>");
-        case Cfg::M2: return skinny_name(M, K, 2, "skinny_kernel<2, 1, 4, 2, true, 6, true>", "skinny_kernel<2, 1, 4, 2, false, 6, true>");
         case Cfg::M2Long: return skinny_name(M, K, 2, "skinny_kernel<2, 1, 8, 3, true, 0, true>", "skinny_kernel<2, 1, 8, 3, false, 0, true>");
-        case Cfg::M4: return skinny_name(M, K, 4, "skinny_kernel<4, 1, 4, 2, true, 0, true>", "skinny_kernel<4, 1, 4, 2, false, 0, true>");
         case Cfg::M4Long: return skinny_name(M, K, 4, "skinny_kernel<4, 1, 8, 3, true, 0, true>", "skinny_kernel<4, 1, 8, 3, false, 0, true>");
         case Cfg::M16: return skinny_name(M, K, 16, "skinny_kernel<16, 1, 4, 2, true, 0, true>", "skinny_kernel<16, 1, 4, 2, false, 0, true>");
         case Cfg::M16Long: return skinny_name(M, K, 16, "skinny_kernel<16, 1, 8, 3, true, 0, true>", "skinny_kernel<16, 1, 8, 3, false, 0, true>");
@@ -1236,11 +1526,14 @@ const char *linear_glu_config_name(int64_t M, int64_t K) {
 
 hipError_t launch_linear_glu(LinearArgs a, hipStream_t s) {
     switch (pick_mk(a.M, a.K)) {
-        case Cfg::M1: return run_skinny<1, 1, 4, 2, 6, true>(a, s);
+        case Cfg::G1: return run_gemv<1, 8, 6, true, 3>(a, s);
+        case Cfg::G1K: return run_gemv<1, 16, 0, true, 2>(a, s);
+        case Cfg::G2: return run_gemv<2, 4, 0, true, 6>(a, s);
+        case Cfg::G2K: return run_gemv<2, 8, 0, true, 4>(a, s);
+        case Cfg::G4: return run_gemv<4, 8, 0, true, 3>(a, s);
+        case Cfg::G4K: return run_gemv<4, 16, 0, true, 2>(a, s);
         case Cfg::M1Long: return run_skinny<1, 1, 8, 3, 0, true>(a, s);
-        case Cfg::M2: return run_skinny<2, 1, 4, 2, 6, true>(a, s);
         case Cfg::M2Long: return run_skinny<2, 1, 8, 3, 0, true>(a, s);
-        case Cfg::M4: return run_skinny<4, 1, 4, 2, 0, true>(a, s);
         case Cfg::M4Long: return run_skinny<4, 1, 8, 3, 0, true>(a, s);
         case Cfg::M16: return run_skinny<16, 1, 4, 2, 0, true>(a, s);
         case Cfg::M16Long: return run_skinny<16, 1, 8, 3, 0, true>(a, s);

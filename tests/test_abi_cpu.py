@@ -128,7 +128,7 @@ def test_linear_swiglu_validates_first(L):
 
 def test_linear_kernel_names(L):
     """The kernel-name query is host logic: invalid arguments give "", decode
-    sizes name a skinny kernel, and above 64 rows the GEMM tile shape follows
+    sizes name a decode kernel (its stage count follows from K), and above 64 rows the GEMM tile shape follows
     the launch's tile count (256 compute units are assumed without a device)."""
     import ctypes
     kn = L.q4_0_linear_kernel
@@ -141,7 +141,14 @@ def test_linear_kernel_names(L):
     assert kn(1, 64, arr(16), 0) == b""                 # no segment
     assert kn(1, 64, arr(*([16] * 9)), 9) == b""        # too many segments
     assert kn(1, 64, None, 1) == b""
-    assert kn(1, 3072, arr(4096, 1024, 1024), 3).startswith(b"skinny_kernel<1, ")
+    assert kn(1, 3072, arr(4096, 1024, 1024), 3) == b"gemv_kernel<1, 8, 3, 6, false>"
+    assert kn(1, 4096, arr(3072), 1) == b"gemv_kernel<1, 16, 2, 0, false>"
+    assert kn(1, 9216, arr(3072), 1) == b"skinny_kernel<1, 1, 16, 2, true, 0, false>"   # long K
+    assert kn(2, 3072, arr(9216, 9216), 2) == b"gemv_kernel<2, 4, 6, 0, false>"
+    assert kn(3, 1280, arr(512), 1) == b"gemv_kernel<4, 8, 2, 0, false>"
+    assert L.q4_0_linear_swiglu_kernel(1, 3072) == b"gemv_kernel<1, 8, 3, 6, true>"
+    assert L.q4_0_linear_swiglu_kernel(2, 4096) == b"gemv_kernel<2, 8, 4, 0, true>"
+    assert L.q4_0_linear_swiglu_kernel(1, 4096) == b"gemv_kernel<1, 16, 2, 0, true>"
     import torch
     if torch.cuda.is_available() and torch.cuda.get_device_properties(0).multi_processor_count != 256:
         return                                          # the tile counts below assume 256 CUs
@@ -154,7 +161,7 @@ def test_linear_kernel_names(L):
     assert kn(40, 3072, arr(131072), 1) == b"gemm_kernel<4, 1, 1, 8, 0, 3>"
     # one row: very tall weights take the stream kernel
     assert kn(1, 3072, arr(131072), 1) == b"skinny_stream_kernel<1, 8, 3, 6>"
-    assert kn(1, 3072, arr(9216, 9216), 2) == b"skinny_kernel<1, 1, 8, 3, true, 6, false>"
+    assert kn(1, 3072, arr(9216, 9216), 2) == b"gemv_kernel<1, 8, 3, 6, false>"
     assert kn(2048, 4096, arr(3072), 1) == b"gemm3_kernel<8, 1, 1, 12, 0, 8, false>"
     assert kn(2048, 3072, arr(3072, 3072, 3072), 3) == b"gemm3_kernel<8, 1, 1, 8, 4, 8, false>"
     assert kn(300, 3072, arr(3072), 1) == b"gemm3_kernel<4, 1, 1, 8, 4, 8, false>"

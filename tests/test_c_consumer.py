@@ -34,7 +34,7 @@ int main(void) {
     if (q4_0_linear_multi(fake, 1, 64, segs, 9, NULL) != Q4_ERR_SEGMENTS) bad |= 128;
     int64_t ns[1] = {4096};
     const char *name = q4_0_linear_kernel(1, 3072, ns, 1);
-    if (strncmp(name, "skinny_kernel<", 14) != 0) bad |= 256;
+    if (strncmp(name, "gemv_kernel<", 12) != 0) bad |= 256;
     printf("c consumer: %s %d\n", name, bad);
     return bad;
 }
@@ -54,4 +54,4 @@ def test_plain_c_program_uses_the_abi(tmp_path):
                     str(src), "-o", str(exe), f"-L{libdir}", "-l:libq4amd.so", f"-Wl,-rpath,{libdir}"], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, (out.returncode, out.stdout, out.stderr)
-    assert "c consumer: skinny_kernel<" in out.stdout
+    assert "c consumer: gemv_kernel<" in out.stdout
