@@ -10,30 +10,29 @@ with every input already resident in HBM.  The step is captured once in a HIP
 graph and replayed; K replays are timed with HIP events on the replay stream.
 
 Printed (one JSON line):
-  value       eff. HBM GB/s of the whole step: algorithmic bytes per step
-              (packed weights + x + y) * K / elapsed
-  decode_m2   the same step at M=2 (the batched CFG pair): us/step and GB/s
-  roofline    the dominant kernel (the M=1 decode kernel) against 8 TB/s:
-              algorithmic bytes of its launches / their summed kernel-own
-              durations, taken with events armed on each launch of the timed
-              steps (q4_0_time_next_launch; an eager pass over the same K steps)
-  prefill     M=2048 through the four decoder shapes: TFLOP/s (2*M*N*K / time)
-              and the GEMM kernel's roofline against 2.5 PFLOP/s bf16
-  swiglu      the fused gate/up + SwiGLU launch (q4_0_linear_swiglu) next to
-              the unfused gate/up launch it replaces, at M = 1, 2 and 2048
-              (kernel-own times; each kind walks the 26 layers' gate/up
-              weights in turn, so every launch streams its weights from HBM)
-  embed       Q4 embedding lookups of 32, 2048 and 16384 random ids from the
-              131072 x 3072 table, packed (q4_0_embed) and as GGUF blocks
-              (q4_0_embed_gguf, under "gguf"): kernel-own time per launch,
-              each after a 512 MiB read (rows from HBM), and GB/s moved
-  lm_head     the same table as the LM head linear at M = 1 and 32 (kernel-own
-              times, each launch after a 512 MiB read so the table comes from HBM)
-  other_workloads  the lone GEMV 3072->4096 at M=1 and the audio linears
-              (5120->3072 and 3072->3072 at M=1505, 1280->5120 and 5120->1280
-              at M=6020), timed like the LM head: median, p10 and p90
-  cpu_baseline  the CPU oracle (dequantize + fp64 matmul) on a bounded sample
-              of the same step, on the host cores
+  value        eff. HBM GB/s of the whole step: algorithmic bytes per step
+               (packed weights + x + y) * K / elapsed
+  roofline     the dominant kernel (the M=1 decode kernel) against 8 TB/s:
+               algorithmic bytes of its launches / their summed kernel-own
+               durations, taken with events armed on each launch of the timed
+               steps (q4_0_time_next_launch; an eager pass over the same K steps)
+  workloads    one record per workload (1 the lone GEMV, 2 the decode step at
+               M=1 and 2, 3 the LM head at M=1 and 32, 4 the M=2048 prefill,
+               5 the audio linears): algorithmic bytes and flops, kernel-time
+               p10/p50/p90, GB/s or TFLOP/s against the roofline, the kernel
+               names, parity of the timed outputs against the oracle on sampled
+               weight rows (max |err|/bound, cosine) and the oracle's own rate on
+               the host cores over a stated sample
+  decode_floor the same 104-launch step with a plain read of the same weight
+               bytes in each launch, and with 104 empty launches: what a step
+               of this launch structure costs without the layer's arithmetic
+  swiglu       the fused gate/up + SwiGLU launch next to the unfused gate/up
+               launch it replaces, at M = 1, 2 and 2048 (kernel-own times)
+  embed        Q4 embedding lookups of 32, 2048 and 16384 random ids from the
+               131072 x 3072 table, packed and as GGUF blocks (key gguf)
+  cpu_baseline the oracle (dequantize + fp64 matmul) over the whole decode step
+               at M=1 on the host cores (workload 2's CPU record)
+  seed, git_rev, host_cores, blas   run metadata
 """
 
 from __future__ import annotations
@@ -341,11 +340,12 @@ def time_single(spec, pw, ms, reps, dev):
     flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
     sink = torch.empty((), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    out = {}
+    out, ys = {}, {}
     for m in ms:
         xb = spec.activations(m)
         x = torch.from_numpy(xb.view(np.int16).copy()).to(dev).view(torch.bfloat16)
         y = torch.empty((m, pw.n), dtype=torch.float32, device=dev)
+        ys[m] = y
         q4.linear(x, pw, y)
         pairs = []
         for _ in range(reps):
@@ -367,10 +367,10 @@ def time_single(spec, pw, ms, reps, dev):
                          "GBs": round(moved / t / 1e9, 1), "frac_of_8TBs": round(moved / t / 1e9 / HBM_PEAK_GBS, 4),
                          "TFLOPs": round(flops(spec, m) / t / 1e12, 2),
                          "frac_of_bf16_peak": round(flops(spec, m) / t / 1e12 / BF16_PEAK_TFLOPS, 4),
-                         "launches": reps}
-        del x, y
+                         "bytes_alg": moved, "flops": flops(spec, m), "launches": reps}
+        del x
     del flush, sink
-    return out
+    return out, ys
 
 
 def kernel_source_digest():
@@ -403,40 +403,124 @@ def measured_traffic(kernel):
     return t.get("hbm_bytes_per_launch")
 
 
-# --------------------------------------------------------- CPU baseline
-def cpu_baseline(specs, budget_s):
-    """The oracle on a bounded sample of the decode step (whole launches,
-    in step order, until the budget is spent), reported as GB/s."""
+# ------------------------------------------------------------- metadata
+def run_meta():
+    """Seed, source revision, host cores and the BLAS the oracle runs on."""
+    info = {"seed": 0, "git_rev": None, "host_cores": len(os.sched_getaffinity(0)), "blas": None}
+    try:
+        with open(os.path.join(ROOT, "q4_weight_only_amd", "_build", "build_info.json")) as f:
+            b = json.load(f)
+        info["git_rev"] = b.get("git_rev")
+        info["source_dirty_at_build"] = b.get("dirty")
+    except (OSError, ValueError):
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = {"vendor": blas[0].get("internal_api"), "version": blas[0].get("version"),
+                            "threads": blas[0].get("num_threads")}
+    except Exception:
+        pass
+    return info
+
+
+# --------------------------------------------------------------- parity
+def parity_rows(spec, si, m, y_dev, w=None, count=48):
+    """The timed output y_dev [m, N] of segment si against the oracle on
+    `count` sampled weight rows (every m row): (max |err|/bound, cosine).  The
+    oracle quantizes those rows itself from the seeded fp32 weights."""
     import numpy as np
 
     from oracle import q4_0_oracle as O
 
+    if w is None:
+        w = spec.weight(si)
+    n = w.shape[0]
+    rng = np.random.default_rng(1000 + si)
+    rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=min(count, n), replace=False)]))
+    blocks = O.quantize(np.ascontiguousarray(w[rows]))
+    ref, bound = O.linear_with_bound(spec.activations(m), blocks, len(rows), spec.K)
+    y = y_dev[:, rows].cpu().numpy().astype(np.float64)
+    ratio = float(np.max(np.abs(y - ref) / bound))
+    cos = float(np.dot(y.ravel(), ref.ravel()) / (np.linalg.norm(y) * np.linalg.norm(ref)))
+    return ratio, cos
+
+
+def parity_record(checks):
+    """Summary of a list of (ratio, cosine) checks."""
+    return {"max_err_over_bound": round(max(r for r, _ in checks), 6),
+            "cosine_min": min(c for _, c in checks), "checks": len(checks), "rows_per_check": 48,
+            "within_bound": bool(all(r <= 1.0 for r, _ in checks))}
+
+
+# ------------------------------------------------------- CPU oracle rate
+def oracle_threads():
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        return max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
     except Exception:
-        threads = len(os.sched_getaffinity(0))
-    done_bytes, elapsed, launches = 0, 0.0, 0
-    for spec in specs:
-        if elapsed >= budget_s:
-            break
-        blocks = [O.quantize(spec.weight(si)) for si in range(len(spec.Ns))]   # untimed input prep
-        xb = spec.activations(1)
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_oracle_rate(jobs, runs, unit, sample):
+    """Time the oracle (dequantize + fp64 matmul, input quantization outside
+    the timer) over `jobs` = [(x_bits, blocks, n, k, amount)], `runs` times;
+    the median rate in `unit` ("GB/s": amount = algorithmic bytes,
+    "GFLOP/s": amount = 2 m n k)."""
+    import numpy as np
+
+    from oracle import q4_0_oracle as O
+
+    rates = []
+    for _ in range(runs):
         t0 = time.perf_counter()
-        for si, n in enumerate(spec.Ns):
-            O.linear(xb, blocks[si], n, spec.K)
-        elapsed += time.perf_counter() - t0
-        done_bytes += algorithmic_bytes(spec, 1)
-        launches += 1
-    return {
-        "value": round(done_bytes / elapsed / 1e9, 3),
-        "unit": "GB/s",
-        "cores": int(threads),
-        "kind": "oracle",
-        "sample": f"first {launches} of the 104 decode-step launches (M=1), dequantize + fp64 matmul, "
-                  f"{elapsed:.1f} s of CPU time",
-    }
+        for xb, blocks, n, k, _amount in jobs:
+            O.linear(xb, blocks, n, k)
+        dt = time.perf_counter() - t0
+        rates.append(sum(j[4] for j in jobs) / dt / 1e9)
+    return {"value": round(float(np.median(rates)), 4), "unit": unit, "runs": runs, "cores": oracle_threads(),
+            "kind": "oracle", "seconds_per_run": round(dt, 2), "sample": sample}
+
+
+# ---------------------------------------------------------- decode floor
+def time_floor(runner, steps, warmup, dev):
+    """The decode step's launch structure without its arithmetic: a graph of
+    one reference read per launch over that launch's weight bytes, and a graph
+    of as many empty launches (reference reads of zero bytes)."""
+    import torch
+
+    import q4_weight_only_amd as q4
+
+    sizes = [spec.weight_bytes() // 16 * 16 for spec, *_ in runner.items]
+    buf = torch.zeros(sum(sizes), dtype=torch.uint8, device=dev)
+    sink = torch.empty(int(q4.lib().q4_0_reference_read_words(max(sizes))), dtype=torch.int32, device=dev)
+    offs = [sum(sizes[:i]) for i in range(len(sizes))]
+
+    class Reads:
+        items = runner.items
+
+        def __init__(self, empty):
+            self.empty = empty
+
+        def step(self):
+            for off, n in zip(offs, sizes):
+                q4.reference_read(buf[off:off + n], 0 if self.empty else n, sink)
+
+    out = {}
+    for key, empty in (("read_us_per_step", False), ("empty_us_per_step", True)):
+        r = Reads(empty)
+        el, g = time_graph(r, steps, warmup, dev)
+        del g
+        out[key] = round(el / steps * 1e6, 1)
+        out[key.replace("_us_per_step", "_p10_p50_p90_us")] = pctl_us(r.step_times)
+    out["launches"] = len(sizes)
+    out["read_bytes_per_step"] = sum(sizes)
+    out["read_GBs"] = round(sum(sizes) / (out["read_us_per_step"] * 1e-6) / 1e9, 1)
+    del buf, sink
+    return out
 
 
 # ------------------------------------------------------------------ main
@@ -449,10 +533,11 @@ def main():
         print(msg, file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np  # noqa: F401
+    import numpy as np
     import torch
 
     import q4_weight_only_amd as q4
+    from oracle import q4_0_oracle as O
     from q4_weight_only_amd import inputs
 
     if not torch.cuda.is_available():
@@ -461,8 +546,10 @@ def main():
     q4.lib()          # fail loudly if the library is not built
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    meta = run_meta()
+    do_cpu = not args.no_cpu_baseline
 
-    # ---- decode step (the headline)
+    # ---- workload 2: the decode step (the headline)
     _, decode = inputs.workload(2)
     specs = [s for s, _ in decode][: 4 * args.layers]
     t0 = time.time()
@@ -536,30 +623,53 @@ def main():
             "graph": "one HIP graph per step",
         },
         "roofline": roofline,
+        **meta,
     }
 
-    # ---- the same step at M=2 (the batched CFG pair of the decode workload)
+    # the same step at M=2 (the batched CFG pair)
     runner2 = Runner(prepared, 2, dev)
     el2, graph2 = time_graph(runner2, args.steps, args.warmup, dev)
     del graph2
     gbs2 = runner2.bytes_per_step() * args.steps / el2 / 1e9
-    out["decode_m2"] = {
-        "workload": "the decode step at M=2 (batched CFG pair), same weights and launches",
-        "us_per_step": round(el2 / args.steps * 1e6, 1),
-        "step_us_p10_p50_p90": pctl_us(runner2.step_times),
-        "value": round(gbs2, 1),
-        "unit": "GB/s",
-        "frac_of_8TBs": round(gbs2 / HBM_PEAK_GBS, 4),
-        "kernels": sorted({q4.linear_kernel(2, spec.K, spec.Ns) for spec, *_ in runner2.items}),
+    log(f"decode M=2: {el2 / args.steps * 1e6:.1f} us/step, {gbs2:.1f} GB/s")
+
+    # parity of the timed outputs (the last replay's): first and last layer
+    checks = []
+    for li in sorted({0, args.layers - 1}):
+        for (spec, pws, xs, ys), (_, _, _, ys2) in zip(runner.items[4 * li:4 * li + 4], runner2.items[4 * li:4 * li + 4]):
+            for si in range(len(spec.Ns)):
+                w = spec.weight(si)
+                checks.append(parity_rows(spec, si, 1, ys[si], w))
+                checks.append(parity_rows(spec, si, 2, ys2[si], w))
+                del w
+    parity2 = parity_record(checks)
+    log(f"decode parity: {parity2}")
+
+    out["decode_floor"] = {
+        "workload": "the decode step's 104 launches, each a plain 16-byte nontemporal read of that launch's "
+                    "weight bytes (q4_0_reference_read), and 104 empty launches; one HIP graph per step",
+        **time_floor(runner, args.steps, args.warmup, dev),
     }
-    log(f"decode M=2: {out['decode_m2']['us_per_step']} us/step, {gbs2:.1f} GB/s")
+    log(f"decode floor: {out['decode_floor']}")
+
+    wl = {}
+    wl["2"] = {
+        "workload": f"{args.layers}-layer decode step, M=1 and M=2 (batched CFG pair), distinct weights per layer",
+        "M=1": {"us_per_step": round(elapsed / args.steps * 1e6, 1), "step_us_p10_p50_p90": pctl_us(runner.step_times),
+                "GBs": round(value, 1), "frac_of_8TBs": round(value / HBM_PEAK_GBS, 4), "bytes_alg": step_bytes,
+                "kernels": sorted({q4.linear_kernel(1, sp.K, sp.Ns) for sp, *_ in runner.items})},
+        "M=2": {"us_per_step": round(el2 / args.steps * 1e6, 1), "step_us_p10_p50_p90": pctl_us(runner2.step_times),
+                "GBs": round(gbs2, 1), "frac_of_8TBs": round(gbs2 / HBM_PEAK_GBS, 4),
+                "bytes_alg": runner2.bytes_per_step(),
+                "kernels": sorted({q4.linear_kernel(2, sp.K, sp.Ns) for sp, *_ in runner2.items})},
+        "parity": parity2,
+    }
     del runner2
 
-    # ---- prefill (M=2048 through the four decoder shapes, layer-0 weights)
+    # ---- workload 4: prefill M=2048 through the four decoder shapes (layer-0 weights)
     if not args.no_prefill:
         _, pre = inputs.workload(4)
         pspecs = [s for s, _ in pre]
-        # the prefill weights are the decode step's layer-0 weights
         layer0 = {s.w_tags: pws for s, pws, _ in prepared}
         pprep = []
         for s in pspecs:
@@ -574,34 +684,49 @@ def main():
         pk_time = sum(sum(d) for d in pdur)
         pk_flops = sum(flops(spec, 2048) * len(d) for (spec, *_), d in zip(prunner.items, pdur))
         pach = pk_flops / pk_time / 1e12
-        # the GEMM tile shape depends on the shape's work tiles: name the one
-        # holding the most kernel time, and every op's
         pk_names = [q4.linear_kernel(2048, spec.K, spec.Ns) for spec, *_ in prunner.items]
         pk_by = collections.Counter()
         for name, d in zip(pk_names, pdur):
             pk_by[name] += sum(d)
-        out["prefill"] = {
-            "value": round(tflops, 2),
-            "unit": "TFLOP/s",
-            "workload": "M=2048 through QKV 3072->6144, O 4096->3072, gate/up 3072->18432, down 9216->3072",
-            "ms_per_step": round(pel / args.prefill_steps * 1e3, 4),
+        pchecks = []
+        for spec, pws, xs, ys in prunner.items:
+            for si in range(len(spec.Ns)):
+                pchecks.append(parity_rows(spec, si, 2048, ys[si]))
+        wl["4"] = {
+            "workload": "prefill M=2048 through QKV 3072->6144, O 4096->3072, gate/up 3072->18432, down 9216->3072",
+            "TFLOPs_per_step": round(tflops, 2),
+            "us_per_step": round(pel / args.prefill_steps * 1e6, 1),
             "step_us_p10_p50_p90": pctl_us(prunner.step_times),
+            "flops": prunner.flops_per_step(),
+            "bytes_alg": prunner.bytes_per_step(),
             "steps": args.prefill_steps,
             "roofline": {
                 "bound": "mfma",
                 "kernel": pk_by.most_common(1)[0][0],
-                "kernels": {spec.name.split(".", 1)[1]: name for (spec, *_), name in zip(prunner.items, pk_names)},
                 "achieved": round(pach, 2),
                 "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s",
                 "frac": round(pach / BF16_PEAK_TFLOPS, 4),
-                "per_op_TFLOPs": {spec.name.split(".", 1)[1]: round(flops(spec, 2048) * len(d) / sum(d) / 1e12, 2)
-                                  for (spec, *_), d in zip(prunner.items, pdur)},
             },
+            "per_op": {spec.name.split(".", 1)[1]: {
+                "kernel": name, "TFLOPs": round(flops(spec, 2048) * len(d) / sum(d) / 1e12, 2),
+                "kernel_us_p10_p50_p90": pctl_us(d), "flops": flops(spec, 2048),
+                "bytes_alg": algorithmic_bytes(spec, 2048)}
+                for (spec, *_), name, d in zip(prunner.items, pk_names, pdur)},
+            "parity": parity_record(pchecks),
         }
+        out["prefill"] = {"value": wl["4"]["TFLOPs_per_step"], "unit": "TFLOP/s", "roofline": wl["4"]["roofline"]}
         log(f"prefill: {tflops:.1f} TFLOP/s (kernel {pach:.1f})")
+        if do_cpu:
+            spec = pspecs[0]
+            rows = 1024
+            blocks = O.quantize(spec.weight(0)[:rows])
+            wl["4"]["cpu"] = cpu_oracle_rate(
+                [(spec.activations(2048), blocks, rows, spec.K, 2 * 2048 * rows * spec.K)], 1, "GFLOP/s",
+                f"M=2048 through the first {rows} rows of the QKV weights (K={spec.K})")
+        del prunner, pprep
 
-    # ---- NEXT-2: fused gate/up + SwiGLU against the unfused gate/up launch
+    # ---- fused gate/up + SwiGLU against the unfused gate/up launch
     if not args.no_swiglu:
         out["swiglu"] = {
             "workload": "decoder gate/up 3072->2x9216 (one weight pair per layer, rotated), "
@@ -610,44 +735,65 @@ def main():
         }
         log(f"swiglu: {out['swiglu']}")
 
-    # ---- NEXT-3: Q4 embedding lookup from the LM head's table
+    # ---- workload 3: the LM head (M = 1 and 32); the same table feeds the embedding lookups
     if not args.no_embed:
         _, lm = inputs.workload(3)
         lm_spec = lm[0][0]
-        wt = torch.from_numpy(lm_spec.weight(0)).to(dev)
+        lm_w = lm_spec.weight(0)
+        wt = torch.from_numpy(lm_w).to(dev)
         lm_blocks = q4.quantize(wt)
         del wt
-        lm_pws = [q4.pack(lm_blocks, lm_spec.Ns[0], lm_spec.K)]
+        lm_pw = q4.pack(lm_blocks, lm_spec.Ns[0], lm_spec.K)
         out["embed"] = {
             "table": f"{lm_spec.Ns[0]}x{lm_spec.K} Q4_0 (the LM head weights), fp32 rows out, random ids; "
                      "packed table (q4_0_embed) and GGUF block order (q4_0_embed_gguf, key gguf)",
-            **time_embed(lm_pws[0], (32, 2048, 16384), 50, dev),
-            "gguf": time_embed(lm_pws[0], (32, 2048, 16384), 50, dev, blocks=lm_blocks),
+            **time_embed(lm_pw, (32, 2048, 16384), 50, dev),
+            "gguf": time_embed(lm_pw, (32, 2048, 16384), 50, dev, blocks=lm_blocks),
         }
         del lm_blocks
         log(f"embed: {out['embed']}")
-        # the same table as the LM head linear (workload 3: M = 1 and 32)
-        out["lm_head"] = {
-            "workload": f"LM head {lm_spec.K}->{lm_spec.Ns[0]} (226 MB of Q4_0), one launch, streamed from HBM",
-            **time_single(lm_spec, lm_pws[0], (1, 32), 20, dev),
-        }
-        log(f"lm_head: {out['lm_head']}")
-        del lm_pws
+        res, ys = time_single(lm_spec, lm_pw, (1, 32), 20, dev)
+        wl["3"] = {"workload": f"LM head {lm_spec.K}->{lm_spec.Ns[0]} (226 MB of Q4_0), one launch, from HBM",
+                   **res, "parity": parity_record([parity_rows(lm_spec, 0, m, ys[m], lm_w) for m in (1, 32)])}
+        log(f"lm_head: {wl['3']}")
+        if do_cpu:
+            rows = 16384
+            blocks = O.quantize(lm_w[:rows])
+            wl["3"]["cpu"] = cpu_oracle_rate(
+                [(lm_spec.activations(1), blocks, rows, lm_spec.K,
+                  rows * lm_spec.K // 32 * 18 + lm_spec.K * 2 + rows * 4)], 3, "GB/s",
+                f"M=1 through the first {rows} of the {lm_spec.Ns[0]} rows (1/8 of the table)")
+        del lm_pw, lm_w, ys
 
-    # ---- the other workloads' single launches: the lone GEMV and the audio
-    # linears (ragged M = 1505 and 6020), each from HBM
+    # ---- workloads 1 and 5: the lone GEMV and the audio linears, each from HBM
     if not args.no_others:
         _, g1 = inputs.workload(1)
         _, a5 = inputs.workload(5)
-        others = {}
-        for spec, ms in g1 + a5:
-            (_, pws, _), = build_device_specs([spec], (), dev)
-            res = time_single(spec, pws[0], ms, 20, dev)
-            for key, r in res.items():
-                others[f"{spec.name} {spec.K}->{spec.Ns[0]} {key}"] = r
-            del pws
-        out["other_workloads"] = others
-        log(f"other workloads: {others}")
+        for key, items in (("1", g1), ("5", a5)):
+            rec, checks, jobs = {}, [], []
+            for spec, ms in items:
+                w = spec.weight(0)
+                (_, pws, _), = build_device_specs([spec], (), dev)
+                res, ys = time_single(spec, pws[0], ms, 20, dev)
+                for mk, r in res.items():
+                    rec[f"{spec.name} {spec.K}->{spec.Ns[0]} {mk}"] = r
+                for m in ms:
+                    checks.append(parity_rows(spec, 0, m, ys[m], w))
+                if do_cpu and key == "1":
+                    jobs.append((spec.activations(1), O.quantize(w), spec.Ns[0], spec.K, algorithmic_bytes(spec, 1)))
+                if do_cpu and key == "5" and spec.name == "adapter":
+                    rows = 512
+                    jobs.append((spec.activations(ms[0]), O.quantize(w[:rows]), rows, spec.K,
+                                 2 * ms[0] * rows * spec.K))
+                del pws, ys, w
+            wl[key] = {"workload": ("one GEMV 3072->4096 at M=1" if key == "1" else
+                                    "audio linears: 5120->3072, 3072->3072 at M=1505; 1280->5120, 5120->1280 at M=6020"),
+                       **rec, "parity": parity_record(checks)}
+            if jobs:
+                wl[key]["cpu"] = (cpu_oracle_rate(jobs, 3, "GB/s", "the whole GEMV") if key == "1" else
+                                  cpu_oracle_rate(jobs, 1, "GFLOP/s", "M=1505 through the first 512 rows of the "
+                                                                         "adapter 5120->3072"))
+            log(f"workload {key}: {wl[key]}")
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -657,10 +803,20 @@ def main():
         torch.cuda.synchronize(dev)
         out["copy_calibration"] = {"bytes_read": 256 << 20, "bytes_written": 256 << 20, "calls": 3}
 
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(specs, args.cpu_seconds)
-        log(f"cpu baseline: {out['cpu_baseline']}")
+    if do_cpu:
+        # the whole decode step at M=1 (input quantization outside the timer)
+        jobs = []
+        for spec in specs:
+            for si, n in enumerate(spec.Ns):
+                jobs.append((spec.activations(1), O.quantize(spec.weight(si)), n, spec.K,
+                             n * spec.K // 32 * 18 + spec.K * 2 // len(spec.Ns) + n * 4))
+        rec = cpu_oracle_rate(jobs, 1, "GB/s", f"the whole {args.layers}-layer decode step at M=1 "
+                                               f"({len(specs)} launches)")
+        wl["2"]["cpu"] = rec
+        out["cpu_baseline"] = rec
+        log(f"cpu baseline: {rec}")
 
+    out["workloads"] = {k: wl[k] for k in sorted(wl)}
     print(json.dumps(out), flush=True)
 
 

@@ -226,8 +226,29 @@ const char *q4_0_linear_swiglu_kernel(int64_t M, int64_t K);
 const char *q4_0_linear_kernel(int64_t M, int64_t K, const int64_t *N, int nseg);
 
 /*
+ * Measurement support: a reference streaming read.  Reads `bytes` bytes at
+ * src (device, 16-byte aligned, bytes a multiple of 16, 0 <= bytes <= 2^40)
+ * with the 16-byte nontemporal loads the linear kernels use for weights, and
+ * does nothing else with them (each workgroup of 256 threads reads 64 KiB and
+ * writes one 32-bit word to sink, so the reads cannot be elided).  With
+ * bytes == 0 it launches one workgroup that reads nothing: the cost of a
+ * launch alone.  sink is device memory of q4_0_reference_read_words(bytes)
+ * 32-bit words, 4-byte aligned.  Not a step of the method: the pages weigh
+ * per-dispatch overheads against the work of short launches (Rust fork,
+ * "Why L0 Is Faster"), and a benchmark uses this to put each linear launch
+ * next to a launch that only moves the same bytes.  Asynchronous on stream;
+ * q4_0_time_next_launch applies to it.  Errors as for the other calls.
+ */
+q4_status q4_0_reference_read(const void *src, int64_t bytes, void *sink, void *stream);
+
+/* 32-bit words of sink a q4_0_reference_read of `bytes` writes (0 if bytes
+ * is invalid). */
+int64_t q4_0_reference_read_words(int64_t bytes);
+
+/*
  * Measurement hook for benchmarks.  Arms the calling thread's next
- * q4_0_linear / q4_0_linear_multi / q4_0_linear_swiglu / q4_0_embed / q4_0_embed_gguf launch so that
+ * q4_0_linear / q4_0_linear_multi / q4_0_linear_swiglu / q4_0_embed / q4_0_embed_gguf /
+ * q4_0_reference_read launch so that
  * its kernel records
  * `start_event` when it starts executing and `stop_event` when it finishes
  * (hipExtLaunchKernelGGL); hipEventElapsedTime on the pair is then that

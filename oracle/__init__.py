@@ -16,6 +16,7 @@ from .q4_0_oracle import (  # noqa: F401
     gguf_encode,
     linear,
     linear_rows,
+    linear_with_bound,
     pack,
     packed_bytes,
     padded_dims,

@@ -156,6 +156,25 @@ def error_bound(x_bits: np.ndarray, blocks: np.ndarray, n: int, k: int,
     return 1e-3 * out + 1e-6
 
 
+def linear_with_bound(x_bits: np.ndarray, blocks: np.ndarray, n: int, k: int,
+                      chunk_rows: int = 8192):
+    """(linear(...), error_bound(...)) with each chunk of rows dequantized
+    once: the same fp64 products and sums as the two functions, for checks
+    of every output element of large matrices."""
+    x = bf16_bits_to_f64(x_bits).reshape(-1, k)
+    ax = np.abs(x)
+    m = x.shape[0]
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(n, k // QK, BLOCK_BYTES)
+    y = np.empty((m, n), dtype=np.float64)
+    s = np.empty((m, n), dtype=np.float64)
+    for r0 in range(0, n, chunk_rows):
+        r1 = min(n, r0 + chunk_rows)
+        w = dequantize(b[r0:r1], r1 - r0, k).astype(np.float64)
+        y[:, r0:r1] = x @ w.T
+        s[:, r0:r1] = ax @ np.abs(w).T
+    return y, 1e-3 * s + 1e-6
+
+
 def linear_rows(x_bits: np.ndarray, blocks: np.ndarray, n: int, k: int,
                 rows: np.ndarray):
     """(y, bound) restricted to the output columns `rows` (sampled checks)."""

@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     pack,
     packed_bytes,
     quantize,
+    reference_read,
     status_str,
     time_next_launch,
     unpack,

@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIG
 EXPORTS = ("q4_status_str", "q4_0_packed_bytes", "q4_0_quantize", "q4_0_quantize_bf16", "q4_0_pack", "q4_0_unpack",
            "q4_0_dequant", "q4_0_linear", "q4_0_linear_multi", "q4_0_time_next_launch",
            "q4_0_linear_kernel", "q4_0_linear_swiglu", "q4_0_linear_swiglu_kernel", "q4_0_embed",
-           "q4_0_embed_gguf")
+           "q4_0_embed_gguf", "q4_0_reference_read", "q4_0_reference_read_words")
 
 
 class Q4Error(ValueError):
@@ -79,6 +79,10 @@ def lib() -> ctypes.CDLL:
             L.q4_0_linear_swiglu_kernel.restype = ctypes.c_char_p
             L.q4_0_time_next_launch.argtypes = [vp, vp]
             L.q4_0_time_next_launch.restype = i32
+            L.q4_0_reference_read.argtypes = [vp, i64, vp, vp]
+            L.q4_0_reference_read.restype = i32
+            L.q4_0_reference_read_words.argtypes = [i64]
+            L.q4_0_reference_read_words.restype = i64
             _lib = L
     return _lib
 
@@ -304,6 +308,29 @@ def linear_swiglu(x: torch.Tensor, gate: PackedWeight, up: PackedWeight,
                                         gate.n, out.data_ptr(), int(dtype == torch.bfloat16), _stream(x.device)),
                "q4_0_linear_swiglu")
     return out
+
+
+def reference_read(src: torch.Tensor, nbytes: int | None = None, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Measurement support: stream nbytes (default: all) of the device tensor
+    src through the reference read kernel; returns the sink words (int32)."""
+    if not src.is_cuda:
+        raise ValueError("src must be a device tensor")
+    total = src.numel() * src.element_size()
+    nbytes = total if nbytes is None else int(nbytes)
+    if nbytes > total:
+        raise ValueError("nbytes exceeds the tensor")
+    words = int(lib().q4_0_reference_read_words(nbytes))
+    if words == 0:
+        raise ValueError("nbytes must be a multiple of 16")
+    if sink is None:
+        sink = torch.empty(words, dtype=torch.int32, device=src.device)
+    if not sink.is_cuda or sink.dtype != torch.int32 or sink.numel() < words:
+        raise ValueError(f"sink must be a device int32 tensor of at least {words} words")
+    _same_device(src, sink, "sink")
+    with torch.cuda.device(src.device):
+        _check(lib().q4_0_reference_read(src.data_ptr(), nbytes, sink.data_ptr(), _stream(src.device)),
+               "q4_0_reference_read")
+    return sink
 
 
 def time_next_launch(start: "torch.cuda.Event", stop: "torch.cuda.Event") -> None:

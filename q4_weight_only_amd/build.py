@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libq4amd.so")
 
-SOURCES = ("q4_0_format.hip", "q4_0_linear.hip", "q4_0_abi.hip")
+SOURCES = ("q4_0_format.hip", "q4_0_linear.hip", "q4_0_measure.hip", "q4_0_abi.hip")
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -61,6 +61,26 @@ def _run(cmd):
     return out
 
 
+BUILD_INFO = os.path.join(BUILD_DIR, "build_info.json")
+
+
+def _write_build_info() -> None:
+    """Record the source revision the library was built from (reports read
+    it where no git checkout exists)."""
+    import json
+
+    def git(*args):
+        try:
+            return subprocess.run(["git", *args], cwd=ROOT, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL,
+                                  text=True, timeout=30).stdout.strip()
+        except (OSError, subprocess.SubprocessError):
+            return ""
+    info = {"git_rev": git("rev-parse", "HEAD") or None,
+            "dirty": bool(git("status", "--porcelain", "--untracked-files=no"))}
+    with open(BUILD_INFO, "w") as f:
+        json.dump(info, f)
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source for gfx950 and link libq4amd.so; return its path."""
     hipcc = _hipcc()
@@ -78,6 +98,7 @@ def build(verbose: bool = False) -> str:
         shown = o if verbose else "\n".join(l for l in o.splitlines() if "warning:" in l)
         if shown.strip():
             print(shown)
+    _write_build_info()
     tmp = LIB + f".tmp{os.getpid()}"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)

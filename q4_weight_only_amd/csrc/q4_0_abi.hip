@@ -192,6 +192,18 @@ const char *q4_0_linear_kernel(int64_t M, int64_t K, const int64_t *N, int nseg)
     return q4::linear_config_name(a);
 }
 
+int64_t q4_0_reference_read_words(int64_t bytes) {
+    if (bytes < 0 || bytes > (int64_t(1) << 40) || bytes % 16) return 0;
+    return q4::reference_read_workgroups(bytes);
+}
+
+q4_status q4_0_reference_read(const void *src, int64_t bytes, void *sink, void *stream) {
+    if (bytes < 0 || bytes > (int64_t(1) << 40) || bytes % 16) return Q4_ERR_SHAPE;
+    if ((bytes > 0 && !src) || !sink) return Q4_ERR_NULL;
+    if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return Q4_ERR_ALIGN;
+    return from_hip(q4::launch_reference_read(src, bytes, static_cast<uint32_t *>(sink), as_stream(stream)));
+}
+
 q4_status q4_0_time_next_launch(void *start_event, void *stop_event) {
     q4::arm_launch_events(reinterpret_cast<hipEvent_t>(start_event), reinterpret_cast<hipEvent_t>(stop_event));
     return Q4_OK;

@@ -72,6 +72,11 @@ const char *linear_config_name(const LinearArgs &a);
 hipError_t launch_linear_glu(LinearArgs a, hipStream_t s);
 const char *linear_glu_config_name(int64_t M, int64_t K);
 
+// Reference streaming read (measurement support): workgroups a read of
+// `bytes` launches, and the launch (sink holds one word per workgroup).
+int64_t reference_read_workgroups(int64_t bytes);
+hipError_t launch_reference_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
+
 // Makes the calling thread's next linear, gated or embedding launch record
 // `start` / `stop` at its kernel's start and end.
 void arm_launch_events(hipEvent_t start, hipEvent_t stop);

@@ -221,3 +221,16 @@ def test_bench_refuses_more_than_one_gpu():
     assert p.returncode == 2
     assert "one GPU only" in p.stderr
     assert p.stdout == ""
+
+
+def test_reference_read_validates_first(L):
+    rr, words = L.q4_0_reference_read, L.q4_0_reference_read_words
+    assert words(0) == 1                       # one workgroup: the launch alone
+    assert words(16) == 1 and words(65536) == 1 and words(65552) == 2
+    assert words(-16) == 0 and words(24) == 0 and words(2**40 + 16) == 0
+    assert rr(FAKE, 24, FAKE, None) == SHAPE            # not a multiple of 16
+    assert rr(FAKE, -16, FAKE, None) == SHAPE
+    assert rr(None, 64, FAKE, None) == NULL
+    assert rr(FAKE, 64, None, None) == NULL
+    assert rr(MISALIGNED + 4, 64, FAKE, None) == ALIGN
+    assert rr(FAKE, 64, FAKE + 2, None) == ALIGN

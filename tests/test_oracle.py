@@ -260,6 +260,17 @@ def test_error_bound_uses_each_blocks_own_scale():
     assert O.linear(x_bits, blocks, 1, 64)[0, 0] == 128.0
 
 
+@pytest.mark.parametrize("m,n,k,chunk", [(3, 40, 256, 16), (1, 7, 96, 8192), (5, 33, 128, 1)])
+def test_linear_with_bound_is_linear_and_error_bound(m, n, k, chunk):
+    """The one-pass helper is exactly the two pinned functions."""
+    rng = np.random.default_rng(m * 1000 + n)
+    blocks = _random_blocks(rng, n, k)
+    x_bits = inputs.activations_bf16((m, k), seed=n, tags=(k,))
+    y, bound = O.linear_with_bound(x_bits, blocks, n, k, chunk_rows=chunk)
+    assert np.array_equal(y, O.linear(x_bits, blocks, n, k, chunk_rows=chunk))
+    assert np.array_equal(bound, O.error_bound(x_bits, blocks, n, k, chunk_rows=chunk))
+
+
 def test_linear_rows_matches_full_linear():
     rng = np.random.default_rng(6)
     n, k = 40, 256
