@@ -21,6 +21,14 @@ from .q4_0_oracle import (  # noqa: F401
     packed_bytes,
     padded_dims,
     quantize,
+    Q41_BLOCK_BYTES,
+    q41_decode,
+    q41_dequantize,
+    q41_encode,
+    q41_linear_with_bound,
+    q41_pack,
+    q41_packed_bytes,
+    q41_quantize,
     silu,
     swiglu,
     swiglu_bound,

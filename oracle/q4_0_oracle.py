@@ -38,6 +38,17 @@ What the oracle computes, and where each step comes from:
   A lookup returns the dequantized rows w[id, :] = (q - 8) * d, exact in
   fp32; an id outside [0, N) gives a row of NaN (a reading: the pages say
   nothing about bad ids, and NaN cannot be mistaken for a real row).
+* The asymmetric variant.  The TTS card ("Voxtral-4B-TTS-2603-ExecuTorch-CUDA",
+  opening paragraph) quantizes the same linears to group-wise asymmetric
+  int4 but gives no group size, zero point or layout.  The reading taken is
+  the asymmetric 4-bit block of the GGUF family the other pages use: 32
+  consecutive k of one row share an fp16 scale d and an fp16 offset m, codes
+  q are 4-bit unsigned and w = q * d + m.  A block is 20 bytes: d, then m
+  (little-endian fp16), then the 16 code bytes in Q4_0's nibble order.  Its
+  quantizer: mn, mx = min and max of the block, d = fp16((mx - mn) / 15),
+  m = fp16(mn), q = clamp(rint((w - m) / d), 0, 15) with the stored fp16
+  values and fp32 arithmetic (q = 0 where d is zero).  Its tolerance takes the
+  magnitudes of both terms: 1e-3 * sum_k |x_k| (|q_k d| + |m|) + 1e-6.
 * The packed device layout (the "CDNA4 tiled layout") is restated here from
   its definition in include/q4_0.h so the device repack can be checked byte
   for byte.  It is a permutation of the GGUF bytes, plus zero padding.
@@ -273,6 +284,90 @@ def quantize(w: np.ndarray) -> np.ndarray:
     return gguf_encode(d16, q)
 
 
+# ---------------------------------------------- asymmetric variant (Q4_1)
+Q41_BLOCK_BYTES = 20     # fp16 d, fp16 m, 16 bytes of nibbles
+
+
+def q41_decode(blocks: np.ndarray, n: int, k: int):
+    """Split asymmetric blocks [n, k/32, 20] into (d fp16, m fp16 [n, k/32],
+    q uint8 [n, k]); code bytes are in Q4_0's nibble order."""
+    if k % QK:
+        raise ValueError("K must be a multiple of 32")
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(n, k // QK, Q41_BLOCK_BYTES)
+    d = b[:, :, 0:2].copy().view("<f2").reshape(n, k // QK)
+    m = b[:, :, 2:4].copy().view("<f2").reshape(n, k // QK)
+    codes = b[:, :, 4:20]
+    q = np.empty((n, k // QK, QK), dtype=np.uint8)
+    q[:, :, 0:16] = codes & 0x0F
+    q[:, :, 16:32] = codes >> 4
+    return d, m, q.reshape(n, k)
+
+
+def q41_encode(d: np.ndarray, m: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Inverse of q41_decode."""
+    n, k = q.shape
+    if k % QK:
+        raise ValueError("K must be a multiple of 32")
+    if q.max(initial=0) > 15:
+        raise ValueError("codes must be 4-bit")
+    qb = q.astype(np.uint8).reshape(n, k // QK, QK)
+    out = np.empty((n, k // QK, Q41_BLOCK_BYTES), dtype=np.uint8)
+    out[:, :, 0:2] = np.ascontiguousarray(d, dtype="<f2").reshape(n, k // QK, 1).view(np.uint8)
+    out[:, :, 2:4] = np.ascontiguousarray(m, dtype="<f2").reshape(n, k // QK, 1).view(np.uint8)
+    out[:, :, 4:20] = qb[:, :, 0:16] | (qb[:, :, 16:32] << 4)
+    return out
+
+
+def q41_dequantize(blocks: np.ndarray, n: int, k: int) -> np.ndarray:
+    """w = q * d + m in fp64 (exact: q * d needs 15 bits, and the sum of two
+    values of fp16 origin fits the 53 bits of fp64)."""
+    d, m, q = q41_decode(blocks, n, k)
+    dd = np.repeat(d.astype(np.float64), QK, axis=1)
+    mm = np.repeat(m.astype(np.float64), QK, axis=1)
+    return q.astype(np.float64) * dd + mm
+
+
+def q41_linear_with_bound(x_bits: np.ndarray, blocks: np.ndarray, n: int, k: int,
+                          chunk_rows: int = 8192):
+    """(y, bound) for the asymmetric format: y = x W^T in fp64 with
+    W = q41_dequantize(...), bound = 1e-3 * sum_k |x_k| (|q_k d| + |m|) + 1e-6."""
+    x = bf16_bits_to_f64(x_bits).reshape(-1, k)
+    ax = np.abs(x)
+    nrow = x.shape[0]
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(n, k // QK, Q41_BLOCK_BYTES)
+    y = np.empty((nrow, n), dtype=np.float64)
+    s = np.empty((nrow, n), dtype=np.float64)
+    for r0 in range(0, n, chunk_rows):
+        r1 = min(n, r0 + chunk_rows)
+        d, m, q = q41_decode(b[r0:r1], r1 - r0, k)
+        dd = np.repeat(d.astype(np.float64), QK, axis=1)
+        mm = np.repeat(m.astype(np.float64), QK, axis=1)
+        qd = q.astype(np.float64) * dd
+        y[:, r0:r1] = x @ (qd + mm).T
+        s[:, r0:r1] = ax @ (np.abs(qd) + np.abs(mm)).T
+    return y, 1e-3 * s + 1e-6
+
+
+def q41_quantize(w: np.ndarray) -> np.ndarray:
+    """fp32 W [n, k] -> asymmetric blocks by the rule in the module header."""
+    w32 = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w32.shape
+    if k % QK:
+        raise ValueError("K must be a multiple of 32")
+    wb = w32.reshape(n, k // QK, QK)
+    mn = wb.min(axis=2)
+    mx = wb.max(axis=2)
+    d16 = ((mx - mn) / np.float32(15.0)).astype(np.float16)    # fp32 divide, RNE to fp16
+    m16 = mn.astype(np.float16)
+    df = d16.astype(np.float32)
+    zero = df == 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.rint((wb - m16.astype(np.float32)[:, :, None]) / df[:, :, None])
+    r = np.clip(r, np.float32(0.0), np.float32(15.0))
+    r = np.where(zero[:, :, None], np.float32(0.0), r)
+    return q41_encode(d16, m16, r.astype(np.uint8).reshape(n, k))
+
+
 # ----------------------------------------------------- device (packed) layout
 def quantize_bf16(w_bits: np.ndarray) -> np.ndarray:
     """bf16 W (bit patterns [n, k]) -> GGUF Q4_0 bytes: each value widened to
@@ -331,3 +426,30 @@ def pack(blocks: np.ndarray, n: int, k: int) -> np.ndarray:
                 nib[off] |= val << 4
         sc[(rt * kt_n + kt) * 64 + r * 4 + i] = dp[:, b]
     return np.concatenate([nib, sc.view(np.uint8)])
+
+
+def q41_packed_bytes(n: int, k: int) -> int:
+    np_, kp = padded_dims(n, k)
+    return np_ * (kp // QK) * Q41_BLOCK_BYTES
+
+
+def q41_pack(blocks: np.ndarray, n: int, k: int) -> np.ndarray:
+    """Asymmetric blocks -> packed device layout (include/q4_0.h, "Packed
+    asymmetric layout"): the nibble and scale planes of pack() for (q, d), the
+    codes stored as q XOR 8 as there, then an offset plane with m at the same
+    element index as d.  Padding blocks have d = m = 0 and q = 8 (all bytes
+    of the nibble plane zero)."""
+    np_, kp = padded_dims(n, k)
+    d, m, q = q41_decode(blocks, n, k)
+    as_q40 = gguf_encode(d, q)                      # (d, q) in the Q4_0 block form
+    front = pack(as_q40, n, k)
+    mp = np.zeros((np_, kp // QK), dtype=np.float16)
+    mp[:n, :k // QK] = m
+    kt_n = kp // TILE_K
+    off = np.zeros(np_ * kp // QK, dtype=np.float16)
+    rows = np.arange(np_)
+    rt, r = rows // TILE_ROWS, rows % TILE_ROWS
+    for b in range(kp // QK):
+        kt, i = b // TILE_BLOCKS, b % TILE_BLOCKS
+        off[(rt * kt_n + kt) * 64 + r * 4 + i] = mp[:, b]
+    return np.concatenate([front, off.view(np.uint8)])
