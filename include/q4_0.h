@@ -226,6 +226,45 @@ const char *q4_0_linear_swiglu_kernel(int64_t M, int64_t K);
 const char *q4_0_linear_kernel(int64_t M, int64_t K, const int64_t *N, int nseg);
 
 /*
+ * The asymmetric variant.  The TTS card ("Voxtral-4B-TTS-2603-ExecuTorch-CUDA",
+ * opening paragraph) quantizes the same linears to group-wise asymmetric
+ * int4 without giving the group size, zero point or layout; the reading
+ * taken is the asymmetric block of the GGUF family: 32 consecutive k of one
+ * row share an fp16 scale d and an fp16 offset m, codes q are 4-bit unsigned,
+ * and w = q * d + m.  A block is 20 bytes: d, then m (little-endian fp16),
+ * then 16 code bytes in the Q4_0 nibble order (byte j: q[j] in bits 0-3,
+ * q[j+16] in bits 4-7).  Block buffers are N * K/32 * 20 bytes.
+ *
+ * Packed asymmetric layout: the Q4_0 packed layout's nibble plane with the
+ * code q itself in each slot (not q XOR 8; padding slots 0), its scale plane
+ * holding d, then an offset plane of the same size holding m at the same
+ * element index as d.  Padding blocks are all zero bytes.  Total size
+ * Np * (Kp / 32) * 20 bytes.
+ *
+ * q4_1_quantize: fp32 W [N, K] (device) -> blocks; per block mn and mx are
+ * the smallest and largest w, d = fp16((mx - mn) / 15) and m = fp16(mn), both
+ * rounded to nearest even, q = clamp(rint((w - m) / d), 0, 15) with the
+ * stored values, fp32 arithmetic and ties to even (q = 0 where d is zero).
+ * Inputs must be finite; bit-for-bit reproducible.
+ * q4_1_pack / q4_1_dequant: as their Q4_0 counterparts (w = q * d + m rounded
+ * once to fp32).
+ * q4_1_linear: y[M, N] (fp32) = x[M, K] (bf16) times W^T.  Each block's
+ * sum of x * q and sum of x are formed by MFMAs and added as d * (sum x q) +
+ * m * (sum x) in fp32, so y is within 1e-3 * sum_k |x_k| (|q_k d| + |m|)
+ * + 1e-6 of the exact result for finite inputs (both terms' magnitudes:
+ * q d and m may cancel in w).  Deterministic.  Sizes, validation and errors
+ * as for q4_0_linear.
+ */
+size_t q4_1_packed_bytes(int64_t N, int64_t K);   /* 0 if N or K is invalid */
+q4_status q4_1_quantize(const float *w, int64_t N, int64_t K, void *blocks, void *stream);
+q4_status q4_1_pack(const void *blocks, int64_t N, int64_t K, void *packed, void *stream);
+q4_status q4_1_dequant(const void *packed, int64_t N, int64_t K, float *w, void *stream);
+q4_status q4_1_linear(const void *x_bf16, int64_t M, const void *packed, int64_t N, int64_t K, float *y,
+                      void *stream);
+/* Name of the kernel q4_1_linear runs for M, K and N (static; "" if invalid). */
+const char *q4_1_linear_kernel(int64_t M, int64_t K, int64_t N);
+
+/*
  * Measurement support: a reference streaming read.  Reads `bytes` bytes at
  * src (device, 16-byte aligned, bytes a multiple of 16, 0 <= bytes <= 2^40)
  * with the 16-byte nontemporal loads the linear kernels use for weights, and
@@ -248,7 +287,7 @@ int64_t q4_0_reference_read_words(int64_t bytes);
 /*
  * Measurement hook for benchmarks.  Arms the calling thread's next
  * q4_0_linear / q4_0_linear_multi / q4_0_linear_swiglu / q4_0_embed / q4_0_embed_gguf /
- * q4_0_reference_read launch so that
+ * q4_1_linear / q4_0_reference_read launch so that
  * its kernel records
  * `start_event` when it starts executing and `stop_event` when it finishes
  * (hipExtLaunchKernelGGL); hipEventElapsedTime on the pair is then that

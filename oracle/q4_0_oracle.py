@@ -435,14 +435,15 @@ def q41_packed_bytes(n: int, k: int) -> int:
 
 def q41_pack(blocks: np.ndarray, n: int, k: int) -> np.ndarray:
     """Asymmetric blocks -> packed device layout (include/q4_0.h, "Packed
-    asymmetric layout"): the nibble and scale planes of pack() for (q, d), the
-    codes stored as q XOR 8 as there, then an offset plane with m at the same
-    element index as d.  Padding blocks have d = m = 0 and q = 8 (all bytes
-    of the nibble plane zero)."""
+    asymmetric layout"): pack()'s nibble and scale planes with the codes q
+    themselves in the nibble slots (not q XOR 8) and d in the scale plane,
+    then an offset plane with m at the same element index as d.  Padding
+    blocks are all zero bytes (d = m = 0, q = 0)."""
     np_, kp = padded_dims(n, k)
     d, m, q = q41_decode(blocks, n, k)
-    as_q40 = gguf_encode(d, q)                      # (d, q) in the Q4_0 block form
-    front = pack(as_q40, n, k)
+    # pack() stores (code XOR 8) and pads with code 8: handing it q XOR 8 puts
+    # q in every real slot and 0 in the padding
+    front = pack(gguf_encode(d, q ^ 8), n, k)
     mp = np.zeros((np_, kp // QK), dtype=np.float16)
     mp[:n, :k // QK] = m
     kt_n = kp // TILE_K

@@ -23,6 +23,13 @@ from ._binding import (  # noqa: F401
     pack,
     packed_bytes,
     quantize,
+    PackedWeightQ41,
+    q41_dequant,
+    q41_linear,
+    q41_linear_kernel,
+    q41_pack,
+    q41_packed_bytes,
+    q41_quantize,
     reference_read,
     status_str,
     time_next_launch,

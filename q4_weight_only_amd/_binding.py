@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIG
 EXPORTS = ("q4_status_str", "q4_0_packed_bytes", "q4_0_quantize", "q4_0_quantize_bf16", "q4_0_pack", "q4_0_unpack",
            "q4_0_dequant", "q4_0_linear", "q4_0_linear_multi", "q4_0_time_next_launch",
            "q4_0_linear_kernel", "q4_0_linear_swiglu", "q4_0_linear_swiglu_kernel", "q4_0_embed",
-           "q4_0_embed_gguf", "q4_0_reference_read", "q4_0_reference_read_words")
+           "q4_0_embed_gguf", "q4_0_reference_read", "q4_0_reference_read_words", "q4_1_packed_bytes",
+           "q4_1_quantize", "q4_1_pack", "q4_1_dequant", "q4_1_linear", "q4_1_linear_kernel")
 
 
 class Q4Error(ValueError):
@@ -83,6 +84,15 @@ def lib() -> ctypes.CDLL:
             L.q4_0_reference_read.restype = i32
             L.q4_0_reference_read_words.argtypes = [i64]
             L.q4_0_reference_read_words.restype = i64
+            L.q4_1_packed_bytes.argtypes = [i64, i64]
+            L.q4_1_packed_bytes.restype = ctypes.c_size_t
+            for fn in (L.q4_1_quantize, L.q4_1_pack, L.q4_1_dequant):
+                fn.argtypes = [vp, i64, i64, vp, vp]
+                fn.restype = i32
+            L.q4_1_linear.argtypes = [vp, i64, vp, i64, i64, vp, vp]
+            L.q4_1_linear.restype = i32
+            L.q4_1_linear_kernel.argtypes = [i64, i64, i64]
+            L.q4_1_linear_kernel.restype = ctypes.c_char_p
             _lib = L
     return _lib
 
@@ -331,6 +341,86 @@ def reference_read(src: torch.Tensor, nbytes: int | None = None, sink: torch.Ten
         _check(lib().q4_0_reference_read(src.data_ptr(), nbytes, sink.data_ptr(), _stream(src.device)),
                "q4_0_reference_read")
     return sink
+
+
+# ------------------------------------------------ the asymmetric variant
+Q41_BLOCK_BYTES = 20
+
+
+class PackedWeightQ41(PackedWeight):
+    """An asymmetric 4-bit weight matrix [N, K] (w = q * d + m per 32-weight
+    block) in the packed asymmetric layout."""
+
+    __slots__ = ()
+
+
+def q41_packed_bytes(n: int, k: int) -> int:
+    return int(lib().q4_1_packed_bytes(int(n), int(k)))
+
+
+def q41_quantize(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 W [N, K] on the device -> asymmetric blocks [N, K/32, 20] (uint8)."""
+    _dev(w, "w", torch.float32)
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    n, k = w.shape
+    if out is None:
+        out = torch.empty((n, max(k // 32, 0), Q41_BLOCK_BYTES), dtype=torch.uint8, device=w.device)
+    _dev(out, "out", torch.uint8)
+    if out.numel() != n * (k // 32) * Q41_BLOCK_BYTES:
+        raise ValueError("out has the wrong size")
+    _same_device(w, out, "out")
+    with torch.cuda.device(w.device):
+        _check(lib().q4_1_quantize(w.data_ptr(), n, k, out.data_ptr(), _stream(w.device)), "q4_1_quantize")
+    return out
+
+
+def q41_pack(blocks: torch.Tensor, n: int, k: int) -> PackedWeightQ41:
+    """Asymmetric blocks (uint8, N*K/32*20 elements, on the device) -> PackedWeightQ41."""
+    _dev(blocks, "blocks", torch.uint8)
+    if blocks.numel() != int(n) * (int(k) // 32) * Q41_BLOCK_BYTES:
+        raise ValueError(f"blocks must hold {int(n) * (int(k) // 32) * Q41_BLOCK_BYTES} bytes for [{n}, {k}]")
+    nbytes = q41_packed_bytes(n, k)
+    if nbytes == 0:
+        raise ValueError(f"invalid shape [{n}, {k}]")
+    out = torch.empty(nbytes, dtype=torch.uint8, device=blocks.device)
+    with torch.cuda.device(blocks.device):
+        _check(lib().q4_1_pack(blocks.data_ptr(), n, k, out.data_ptr(), _stream(blocks.device)), "q4_1_pack")
+    return PackedWeightQ41(out, n, k)
+
+
+def q41_dequant(pw: PackedWeightQ41) -> torch.Tensor:
+    out = torch.empty((pw.n, pw.k), dtype=torch.float32, device=pw.device)
+    with torch.cuda.device(pw.device):
+        _check(lib().q4_1_dequant(pw.data.data_ptr(), pw.n, pw.k, out.data_ptr(), _stream(pw.device)),
+               "q4_1_dequant")
+    return out
+
+
+def q41_linear(x: torch.Tensor, pw: PackedWeightQ41, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y [M, N] fp32 = x [M, K] bf16 times W^T for an asymmetric packed W."""
+    if not isinstance(pw, PackedWeightQ41):
+        raise ValueError("pw must be an asymmetric packed weight (q41_pack)")
+    _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2 or x.shape[1] != pw.k:
+        raise ValueError(f"x must be [M, {pw.k}]")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, pw.n), dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    if tuple(out.shape) != (m, pw.n):
+        raise ValueError("out has the wrong shape")
+    _same_device(x, pw.data, "pw")
+    _same_device(x, out, "out")
+    with torch.cuda.device(x.device):
+        _check(lib().q4_1_linear(x.data_ptr(), m, pw.data.data_ptr(), pw.n, pw.k, out.data_ptr(), _stream(x.device)),
+               "q4_1_linear")
+    return out
+
+
+def q41_linear_kernel(m: int, k: int, n: int) -> str:
+    """Name of the kernel q4_1_linear runs for (M, K, N)."""
+    return lib().q4_1_linear_kernel(int(m), int(k), int(n)).decode()
 
 
 def time_next_launch(start: "torch.cuda.Event", stop: "torch.cuda.Event") -> None:

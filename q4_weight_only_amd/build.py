@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libq4amd.so")
 
-SOURCES = ("q4_0_format.hip", "q4_0_linear.hip", "q4_0_measure.hip", "q4_0_abi.hip")
+SOURCES = ("q4_0_format.hip", "q4_1_format.hip", "q4_0_linear.hip", "q4_0_measure.hip", "q4_0_abi.hip")
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

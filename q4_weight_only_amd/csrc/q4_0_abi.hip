@@ -27,6 +27,7 @@ q4::Segment make_segment(const void *packed, int64_t N, int64_t K, float *y) {
     q4::Segment sg;
     sg.nib = static_cast<const uint8_t *>(packed);
     sg.scales = reinterpret_cast<const uint16_t *>(static_cast<const uint8_t *>(packed) + pd.nib_bytes());
+    sg.offsets = nullptr;
     sg.y = y;
     sg.N = static_cast<int32_t>(N);
     sg.RT = static_cast<int32_t>(pd.RT);
@@ -190,6 +191,66 @@ const char *q4_0_linear_kernel(int64_t M, int64_t K, const int64_t *N, int nseg)
     }
     a.KT = static_cast<int32_t>(q4::round_up(K, q4::kTileK) / q4::kTileK);
     return q4::linear_config_name(a);
+}
+
+size_t q4_1_packed_bytes(int64_t N, int64_t K) {
+    if (!shape_ok(N, K)) return 0;
+    return static_cast<size_t>(q4::PackedDims(N, K).q41_total_bytes());
+}
+
+q4_status q4_1_quantize(const float *w, int64_t N, int64_t K, void *blocks, void *stream) {
+    if (!shape_ok(N, K)) return Q4_ERR_SHAPE;
+    if (!w || !blocks) return Q4_ERR_NULL;
+    if (!aligned16(w) || !aligned16(blocks)) return Q4_ERR_ALIGN;
+    return from_hip(q4::launch_q41_quantize(w, N, K, static_cast<uint8_t *>(blocks), as_stream(stream)));
+}
+
+q4_status q4_1_pack(const void *blocks, int64_t N, int64_t K, void *packed, void *stream) {
+    if (!shape_ok(N, K)) return Q4_ERR_SHAPE;
+    if (!blocks || !packed) return Q4_ERR_NULL;
+    if (!aligned16(blocks) || !aligned16(packed)) return Q4_ERR_ALIGN;
+    return from_hip(q4::launch_q41_pack(static_cast<const uint8_t *>(blocks), N, K, static_cast<uint8_t *>(packed),
+                                        as_stream(stream)));
+}
+
+q4_status q4_1_dequant(const void *packed, int64_t N, int64_t K, float *w, void *stream) {
+    if (!shape_ok(N, K)) return Q4_ERR_SHAPE;
+    if (!w || !packed) return Q4_ERR_NULL;
+    if (!aligned16(w) || !aligned16(packed)) return Q4_ERR_ALIGN;
+    return from_hip(q4::launch_q41_dequant(static_cast<const uint8_t *>(packed), N, K, w, as_stream(stream)));
+}
+
+namespace {
+q4::LinearArgs q41_args(const void *x_bf16, int64_t M, const void *packed, int64_t N, int64_t K, float *y) {
+    q4::LinearArgs a;
+    a.x = static_cast<const uint16_t *>(x_bf16);
+    a.M = static_cast<int32_t>(M);
+    a.K = static_cast<int32_t>(K);
+    a.KT = static_cast<int32_t>(q4::round_up(K, q4::kTileK) / q4::kTileK);
+    a.nseg = 1;
+    a.y_bf16 = 0;
+    for (int i = 0; i < q4::kMaxSegments; ++i) a.seg[i] = q4::Segment{};
+    const q4::PackedDims pd(N, K);
+    a.seg[0] = make_segment(packed, N, K, y);
+    a.seg[0].offsets = reinterpret_cast<const uint16_t *>(static_cast<const uint8_t *>(packed) + pd.nib_bytes() +
+                                                          pd.RT * pd.KT * q4::kTileScales * 2);
+    return a;
+}
+}  // namespace
+
+q4_status q4_1_linear(const void *x_bf16, int64_t M, const void *packed, int64_t N, int64_t K, float *y,
+                      void *stream) {
+    if (M < 0 || M > kMaxM || !shape_ok(N, K)) return Q4_ERR_SHAPE;
+    if (M == 0) return Q4_OK;
+    if (!x_bf16 || !packed || !y) return Q4_ERR_NULL;
+    if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(y)) return Q4_ERR_ALIGN;
+    return from_hip(q4::launch_linear_q41(q41_args(x_bf16, M, packed, N, K, y), as_stream(stream)));
+}
+
+const char *q4_1_linear_kernel(int64_t M, int64_t K, int64_t N) {
+    if (M < 1 || M > kMaxM || !shape_ok(N, K)) return "";
+    q4::LinearArgs a = q41_args(nullptr, M, nullptr, N, K, nullptr);
+    return q4::linear_q41_config_name(a);
 }
 
 int64_t q4_0_reference_read_words(int64_t bytes) {

@@ -16,6 +16,7 @@ constexpr int kTileK = 128;        // k per super-tile
 constexpr int kTileNibBytes = 1024;
 constexpr int kTileScales = 64;    // fp16 scales per super-tile
 constexpr int kMaxSegments = 8;
+constexpr int kQ41BlockBytes = 20; // asymmetric block: fp16 d, fp16 m + 16 code bytes
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
@@ -26,12 +27,14 @@ struct PackedDims {
           KT(round_up(k, kTileK) / kTileK), RT(round_up(n, kTileRows) / kTileRows) {}
     int64_t nib_bytes() const { return Np * Kp / 2; }
     int64_t total_bytes() const { return Np * (Kp / kQK) * kBlockBytes; }
+    int64_t q41_total_bytes() const { return Np * (Kp / kQK) * kQ41BlockBytes; }
 };
 
 // One weight matrix of a (possibly fused) launch, as the kernels see it.
 struct Segment {
     const uint8_t *nib;      // nibble plane
     const uint16_t *scales;  // scale plane (fp16 bits)
+    const uint16_t *offsets; // offset plane (fp16 bits; asymmetric layout only)
     float *y;                // [M, N] row-major
     int32_t N;               // true rows of W (= columns of y)
     int32_t RT;              // padded rows / 16
@@ -54,6 +57,9 @@ hipError_t launch_quantize_bf16(const uint16_t *w, int64_t N, int64_t K, uint8_t
 hipError_t launch_pack(const uint8_t *gguf, int64_t N, int64_t K, uint8_t *packed, hipStream_t s);
 hipError_t launch_unpack(const uint8_t *packed, int64_t N, int64_t K, uint8_t *gguf, hipStream_t s);
 hipError_t launch_dequant(const uint8_t *packed, int64_t N, int64_t K, float *w, hipStream_t s);
+hipError_t launch_q41_quantize(const float *w, int64_t N, int64_t K, uint8_t *out, hipStream_t s);
+hipError_t launch_q41_pack(const uint8_t *blocks, int64_t N, int64_t K, uint8_t *packed, hipStream_t s);
+hipError_t launch_q41_dequant(const uint8_t *packed, int64_t N, int64_t K, float *w, hipStream_t s);
 hipError_t launch_embed(const uint8_t *packed, int64_t N, int64_t K, const int32_t *ids, int64_t n_ids,
                         float *out, hipStream_t s);
 hipError_t launch_embed_gguf(const uint8_t *gguf, int64_t N, int64_t K, const int32_t *ids, int64_t n_ids,
@@ -66,6 +72,10 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s);
 // Name of the kernel instantiation launch_linear picks for a launch (M, K
 // and, above 64 rows, the segments' RT and the current device's CU count).
 const char *linear_config_name(const LinearArgs &a);
+
+// The asymmetric layout's linear (one segment, offsets set).
+hipError_t launch_linear_q41(LinearArgs a, hipStream_t s);
+const char *linear_q41_config_name(const LinearArgs &a);
 
 // The gated launch: segment 0 is gate (its y receives silu(gate) * up),
 // segment 1 is up, of the same shape; tile_begin is filled in here too.

@@ -82,6 +82,30 @@ __device__ __forceinline__ bf16x8 decode_piece(uint32_t w) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// 8 unsigned codes (the asymmetric layout: element 2p in the low nibble of
+// byte p, 2p+1 in the high nibble) -> bf16x8 of q in element order.  Exact.
+__device__ __forceinline__ bf16x8 decode_piece_u(uint32_t w) {
+    uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    // hide the masks from the combiner, so each code is one byte-select
+    // conversion (v_cvt_f32_ubyte0..3) of a masked word, not a bit-field
+    // extract followed by a conversion
+    asm("" : "+v"(lo), "+v"(hi));
+    bf16x2 p[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        p[b] = __builtin_convertvector((floatx2){static_cast<float>((lo >> (8 * b)) & 0xFFu),
+                                                 static_cast<float>((hi >> (8 * b)) & 0xFFu)}, bf16x2);
+    const bf16x4 l = __builtin_shufflevector(p[0], p[1], 0, 1, 2, 3);
+    const bf16x4 h = __builtin_shufflevector(p[2], p[3], 0, 1, 2, 3);
+    return __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// An MFMA B operand of ones: the product is the block's sum of x per row.
+__device__ __forceinline__ bf16x8 bf16_ones() {
+    const __bf16 one = static_cast<__bf16>(1.0f);
+    return (bf16x8){one, one, one, one, one, one, one, one};
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
     return __half2float(__ushort_as_half(static_cast<unsigned short>(bits16)));
 }
@@ -371,10 +395,15 @@ constexpr int kNonTemporal = 2;           // cache-policy bit of a buffer load: 
 // waves and bytes per wave.  A column's result does not depend on its
 // neighbours, so g and u are the plain launch's values; after the reduction
 // lane c < 8 takes u from lane c + 8 and stores silu(g) * u.
-template <int MROWS, int WK, int NS, int WPE, bool GLU>
+//
+// ASYM: the asymmetric layout (codes q, scale d, offset m; w = q d + m).  The
+// codes are decoded as q itself, a second MFMA against ones gives the
+// block's sum S of x, and each block adds d * D + m * S (no final * 16).
+template <int MROWS, int WK, int NS, int WPE, bool GLU, bool ASYM = false>
 __global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
 void gemv_kernel(const LinearArgs a) {
     static_assert(MROWS >= 1 && MROWS <= 16, "one 16-row m-tile");
+    static_assert(!(GLU && ASYM), "no gated launch of the asymmetric layout");
     constexpr int REGS = MROWS < 4 ? MROWS : 4;
     constexpr int kThreads = 64 * WK;
     extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
@@ -401,7 +430,7 @@ void gemv_kernel(const LinearArgs a) {
     // never stored)
     const int rt = rt0 < sg.RT ? rt0 : sg.RT - 1;
     const int64_t T0 = static_cast<int64_t>(rt) * KT;
-    __amdgpu_buffer_rsrc_t nib_rsrc, sc_rsrc;
+    __amdgpu_buffer_rsrc_t nib_rsrc, sc_rsrc, off_rsrc;
     const uint8_t *nib_lane = nullptr;
     const uint8_t *sc_lane = nullptr;
     if constexpr (GLU) {
@@ -416,6 +445,9 @@ void gemv_kernel(const LinearArgs a) {
                                                      KT * kTileNibBytes, kBufferRsrcWord3);
         sc_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(sg.scales + T0 * kTileScales), 0,
                                                     KT * kTileScales * 2, kBufferRsrcWord3);
+        if constexpr (ASYM)
+            off_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(sg.offsets + T0 * kTileScales), 0,
+                                                         KT * kTileScales * 2, kBufferRsrcWord3);
     }
 
     // 1. x first: every chunk of this thread, zero past K (a chunk past the
@@ -439,6 +471,7 @@ void gemv_kernel(const LinearArgs a) {
     // 2. then every weight stage of this wave, each one's codes then scales
     u32x4 nib[NS];
     u32x2 sc[NS];
+    u32x2 mo[ASYM ? NS : 1];
     int ktj[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
@@ -454,6 +487,9 @@ void gemv_kernel(const LinearArgs a) {
                                                    nib_rsrc, lane * 16, ktj[j] * kTileNibBytes, kNonTemporal));
             sc[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
                                                   sc_rsrc, nl * 8, ktj[j] * kTileScales * 2, kNonTemporal));
+            if constexpr (ASYM)
+                mo[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                      off_rsrc, nl * 8, ktj[j] * kTileScales * 2, kNonTemporal));
         }
         __builtin_amdgcn_sched_barrier(0);   // stages go out in order
     }
@@ -472,11 +508,17 @@ void gemv_kernel(const LinearArgs a) {
         for (int i = 0; i < kTileBlocks; ++i) {
             const int b = ktj[j] * kTileBlocks + i;
             const bf16x8 A = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xs + a_off + b * kQK * 2));
-            const bf16x8 B = decode_piece(piece_of(nib[j], i));
+            const bf16x8 B = ASYM ? decode_piece_u(piece_of(nib[j], i)) : decode_piece(piece_of(nib[j], i));
             const float d = live ? scale_of(sc[j], i) : 0.0f;
             const floatx4 D = mfma_block(A, B);
 #pragma unroll
             for (int r = 0; r < REGS; ++r) acc[r] = fmaf(d, D[r], acc[r]);
+            if constexpr (ASYM) {
+                const float m = live ? scale_of(mo[j], i) : 0.0f;
+                const floatx4 S = mfma_block(A, bf16_ones());
+#pragma unroll
+                for (int r = 0; r < REGS; ++r) acc[r] = fmaf(m, S[r], acc[r]);
+            }
         }
     }
 
@@ -511,7 +553,7 @@ void gemv_kernel(const LinearArgs a) {
 #pragma unroll
         for (int r = 0; r < REGS; ++r) {
             const int m = 4 * g + r;
-            if (m < a.M) sg.y[static_cast<int64_t>(m) * sg.N + n] = acc[r] * 16.0f;
+            if (m < a.M) sg.y[static_cast<int64_t>(m) * sg.N + n] = ASYM ? acc[r] : acc[r] * 16.0f;
         }
     }
 }
@@ -820,9 +862,6 @@ void gemm_kernel(const LinearArgs a) {
 }
 
 // ------------------------------------------------------------------- gemm3
-#ifndef GEMM_BATCH
-#define GEMM_BATCH 1
-#endif
 // Prefill-sized M with register tiles of MT x NT MFMA tiles per wave.  The
 // x tile of the next 128-k step is staged a quarter per block step (so the
 // staging registers stay few) into the other LDS buffer; the rescale of
@@ -854,9 +893,14 @@ struct Gemm3Cfg {
 // row run gate rows, the last WN / 2 the same rows of up, each exactly as a
 // plain launch would; the up waves hand their results to the gate waves
 // through LDS for the silu(gate) * up epilogue.
-template <int MT, int NT, int WM, int WN, int WPE, int GM, bool GLU>
+//
+// ASYM: the asymmetric layout, as in gemv_kernel: codes decoded as q, the
+// block sums of x from an MFMA against ones (once per m-tile and block), and
+// d * D + m * S added per block.
+template <int MT, int NT, int WM, int WN, int WPE, int GM, bool GLU, bool ASYM = false>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
 void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
+    static_assert(!(GLU && ASYM), "no gated launch of the asymmetric layout");
     using C = Gemm3Cfg<MT, NT, WM, WN>;
     constexpr int BM = C::BM, NPT = C::kAPerThread;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * 256];
@@ -924,7 +968,7 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
     // ---- weights: this wave's NT tiles, straight into registers.  Each tile
     // row's planes are a buffer resource (wave-uniform, in SGPRs) read at a
     // per-lane offset shared by all tiles, so the addresses cost no VGPRs.
-    __amdgpu_buffer_rsrc_t nib_rsrc[NT], sc_rsrc[NT];
+    __amdgpu_buffer_rsrc_t nib_rsrc[NT], sc_rsrc[NT], off_rsrc[ASYM ? NT : 1];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int rt = rt_base + nt < src.RT ? rt_base + nt : src.RT - 1;
@@ -933,17 +977,23 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
                                                          KT * kTileNibBytes, kBufferRsrcWord3);
         sc_rsrc[nt] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(src.scales + T0 * kTileScales), 0,
                                                         KT * kTileScales * 2, kBufferRsrcWord3);
+        if constexpr (ASYM)
+            off_rsrc[nt] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(src.offsets + T0 * kTileScales),
+                                                             0, KT * kTileScales * 2, kBufferRsrcWord3);
     }
     const int nib_lane = lane * 16, sc_lane = nl * 8;
     struct BStage {
         u32x4 nib[NT];
         u32x2 sc[NT];
+        u32x2 off[ASYM ? NT : 1];
     };
     auto load_b = [&](BStage &S, int kt) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             S.nib[nt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(nib_rsrc[nt], nib_lane, kt * kTileNibBytes, 0));
             S.sc[nt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(sc_rsrc[nt], sc_lane, kt * kTileScales * 2, 0));
+            if constexpr (ASYM)
+                S.off[nt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(off_rsrc[nt], sc_lane, kt * kTileScales * 2, 0));
         }
     };
 
@@ -961,25 +1011,29 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
             A[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(tile + (a_row0 + 16 * mt) * 256 + sw));
+        if constexpr (ASYM) {
+            floatx4 Sx[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) Sx[mt] = mfma_block(A[mt], bf16_ones());
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const bf16x8 B = decode_piece_u(piece_of(S.nib[nt], i));
+                const float d = scale_of(S.sc[nt], i), m = scale_of(S.off[nt], i);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const floatx4 D = mfma_block(A[mt], B);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        acc[mt][nt][r] = fmaf(d, D[r], acc[mt][nt][r]);
+                        acc[mt][nt][r] = fmaf(m, Sx[mt][r], acc[mt][nt][r]);
+                    }
+                }
+            }
+        } else
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const bf16x8 B = decode_piece(piece_of(S.nib[nt], i));
             const float d = scale_of(S.sc[nt], i);
-#if GEMM_BATCH > 1
-            constexpr int BT = GEMM_BATCH < MT ? GEMM_BATCH : MT;
-#pragma unroll
-            for (int mb = 0; mb < MT; mb += BT) {
-                floatx4 D[BT];
-#pragma unroll
-                for (int u = 0; u < BT; ++u) D[u] = mfma_block(A[mb + u], B);
-                __builtin_amdgcn_sched_group_barrier(0x008, BT, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 4 * BT, 0);
-#pragma unroll
-                for (int u = 0; u < BT; ++u)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[mb + u][nt][r] = fmaf(d, D[u][r], acc[mb + u][nt][r]);
-            }
-#else
             // each MFMA's rescale is issued after the next MFMA, so the FMAs
             // never wait on a result still in the matrix pipe
             floatx4 D[MT];
@@ -992,7 +1046,6 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[MT - 1][nt][r] = fmaf(d, D[MT - 1][r], acc[MT - 1][nt][r]);
-#endif
         }
         // blocks in groups: within a group the compiler may pull a block's x
         // reads up among the previous block's MFMAs (hiding their LDS
@@ -1073,7 +1126,7 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + (wm * MT + mt) * 16 + 4 * g + r;
                 if (m >= a.M) continue;
-                const float v = acc[mt][nt][r] * 16.0f;
+                const float v = ASYM ? acc[mt][nt][r] : acc[mt][nt][r] * 16.0f;
                 if constexpr (GLU)
                     store_out(a, sg, static_cast<int64_t>(m) * sg.N + n,
                               silu_f32(v) * (xch[((mt * NT + nt) * 4 + r) * 64 + lane] * 16.0f));
@@ -1235,9 +1288,9 @@ hipError_t run_skinny(LinearArgs a, hipStream_t s) {
 constexpr int kGemvMaxStages = 6;
 inline int gemv_stages(const LinearArgs &a, int wk) { return (a.KT + wk - 1) / wk; }
 
-template <int MROWS, int WK, int NS, int WPE, bool GLU>
+template <int MROWS, int WK, int NS, int WPE, bool GLU, bool ASYM>
 hipError_t launch_gemv_ns(const LinearArgs &a, int tiles, uint32_t lds, hipStream_t s) {
-    auto kernel = gemv_kernel<MROWS, WK, NS, WPE, GLU>;
+    auto kernel = gemv_kernel<MROWS, WK, NS, WPE, GLU, ASYM>;
     static std::atomic<uint64_t> lds_allowed{0};
     const hipError_t e = allow_dynamic_lds(kernel, lds_allowed);
     if (e != hipSuccess) return e;
@@ -1246,18 +1299,18 @@ hipError_t launch_gemv_ns(const LinearArgs &a, int tiles, uint32_t lds, hipStrea
 
 // NSMAX: the most stages the dispatch can ask of this configuration (only
 // those stage counts are instantiated).
-template <int MROWS, int WK, int WPE, bool GLU, int NSMAX>
+template <int MROWS, int WK, int WPE, bool GLU, int NSMAX, bool ASYM = false>
 hipError_t run_gemv(LinearArgs a, hipStream_t s) {
     static_assert(NSMAX >= 1 && NSMAX <= kGemvMaxStages, "stage count");
     const int tiles = assign_tiles<GLU>(a, 1) * (GLU ? 2 : 1);   // gated: two 8-row halves per tile
     const uint32_t lds = static_cast<uint32_t>(skinny_x_bytes(a.M, a.K, MROWS)) + 16;   // + the pad slot
     switch (gemv_stages(a, WK)) {
-        case 1: return launch_gemv_ns<MROWS, WK, 1, WPE, GLU>(a, tiles, lds, s);
-        case 2: if constexpr (NSMAX >= 2) return launch_gemv_ns<MROWS, WK, 2, WPE, GLU>(a, tiles, lds, s); break;
-        case 3: if constexpr (NSMAX >= 3) return launch_gemv_ns<MROWS, WK, 3, WPE, GLU>(a, tiles, lds, s); break;
-        case 4: if constexpr (NSMAX >= 4) return launch_gemv_ns<MROWS, WK, 4, WPE, GLU>(a, tiles, lds, s); break;
-        case 5: if constexpr (NSMAX >= 5) return launch_gemv_ns<MROWS, WK, 5, WPE, GLU>(a, tiles, lds, s); break;
-        case 6: if constexpr (NSMAX >= 6) return launch_gemv_ns<MROWS, WK, 6, WPE, GLU>(a, tiles, lds, s); break;
+        case 1: return launch_gemv_ns<MROWS, WK, 1, WPE, GLU, ASYM>(a, tiles, lds, s);
+        case 2: if constexpr (NSMAX >= 2) return launch_gemv_ns<MROWS, WK, 2, WPE, GLU, ASYM>(a, tiles, lds, s); break;
+        case 3: if constexpr (NSMAX >= 3) return launch_gemv_ns<MROWS, WK, 3, WPE, GLU, ASYM>(a, tiles, lds, s); break;
+        case 4: if constexpr (NSMAX >= 4) return launch_gemv_ns<MROWS, WK, 4, WPE, GLU, ASYM>(a, tiles, lds, s); break;
+        case 5: if constexpr (NSMAX >= 5) return launch_gemv_ns<MROWS, WK, 5, WPE, GLU, ASYM>(a, tiles, lds, s); break;
+        case 6: if constexpr (NSMAX >= 6) return launch_gemv_ns<MROWS, WK, 6, WPE, GLU, ASYM>(a, tiles, lds, s); break;
         default: break;
     }
     return hipErrorInvalidValue;   // the dispatch never asks for more than NSMAX stages
@@ -1271,14 +1324,14 @@ hipError_t run_gemm(LinearArgs a, hipStream_t s) {
     return launch_kernel(gemm_kernel<MT, NT, WM, WN, WPE, PB>, dim3(tiles, mtiles), dim3(C::kThreads), 0, s, a);
 }
 
-template <int MT, int NT, int WM, int WN, int WPE = 0, int GM = 8, bool GLU = false>
+template <int MT, int NT, int WM, int WN, int WPE = 0, int GM = 8, bool GLU = false, bool ASYM = false>
 hipError_t run_gemm3(LinearArgs a, hipStream_t s) {
     using C = Gemm3Cfg<MT, NT, WM, WN>;
     const int ntiles = assign_tiles<GLU>(a, NT * (GLU ? WN / 2 : WN));
     const int mtiles = static_cast<int>((a.M + C::BM - 1) / C::BM);
     const int64_t total = static_cast<int64_t>(ntiles) * mtiles;
     if (total > 0x7fffffff) return hipErrorInvalidValue;
-    auto kernel = gemm3_kernel<MT, NT, WM, WN, WPE, GM, GLU>;
+    auto kernel = gemm3_kernel<MT, NT, WM, WN, WPE, GM, GLU, ASYM>;
     const dim3 grid(static_cast<uint32_t>(total)), block(C::kThreads);
     if (t_start_event || t_stop_event) {
         hipEvent_t start = t_start_event, stop = t_stop_event;
@@ -1386,17 +1439,22 @@ Cfg pick_17_64(const LinearArgs &a, Cfg gemm) {
     return rts >= cus ? Cfg::M32Split2 : Cfg::M32Split;
 }
 
+// GEMM tile shape above 64 rows by wave quantization (see the table above).
+Cfg gemm_shape(const LinearArgs &a) {
+    const int64_t cus = device_cus();
+    auto cost = [&](int bm, int bn, int64_t unit) { return (gemm_tiles(a, bm, bn) + cus - 1) / cus * unit; };
+    const int64_t c64 = cost(64, 128, 30), c128 = cost(128, 128, 50), c128w = cost(128, 192, 85);
+    if (c128 <= c64 && c128 <= c128w) return Cfg::Gemm128;
+    return c64 <= c128w ? Cfg::Gemm64 : Cfg::Gemm128W;
+}
+
 Cfg pick(const LinearArgs &a) {
     if (a.M <= 64) {
         const Cfg c = pick_mk(a.M, a.K);
         if (c == Cfg::M32 || c == Cfg::M64) return pick_17_64(a, c);
         return c == Cfg::G1 && stream_m1(a) ? Cfg::M1Stream : c;
     }
-    const int64_t cus = device_cus();
-    auto cost = [&](int bm, int bn, int64_t unit) { return (gemm_tiles(a, bm, bn) + cus - 1) / cus * unit; };
-    const int64_t c64 = cost(64, 128, 30), c128 = cost(128, 128, 50), c128w = cost(128, 192, 85);
-    if (c128 <= c64 && c128 <= c128w) return Cfg::Gemm128;
-    return c64 <= c128w ? Cfg::Gemm64 : Cfg::Gemm128W;
+    return gemm_shape(a);
 }
 
 // Name of a skinny_kernel instantiation, with the x staging the launch picks.
@@ -1407,7 +1465,7 @@ const char *skinny_name(int64_t M, int64_t K, int mrows_max, const char *lds_nam
 
 // Name of a gemv_kernel instantiation (static string): the stage count
 // follows from K, so the names come from a table built once.
-const char *gemv_name(int mrows, int wk, int ns, int wpe, bool glu) {
+const char *gemv_name(int mrows, int wk, int ns, int wpe, bool glu, bool asym = false) {
     static const std::vector<std::string> table = [] {
         std::vector<std::string> t;
         for (int m : {1, 2, 4})
@@ -1415,14 +1473,16 @@ const char *gemv_name(int mrows, int wk, int ns, int wpe, bool glu) {
                 for (int n = 1; n <= kGemvMaxStages; ++n)
                     for (int e : {0, 6})
                         for (int gl : {0, 1})
-                            t.push_back("gemv_kernel<" + std::to_string(m) + ", " + std::to_string(w) + ", " +
-                                        std::to_string(n) + ", " + std::to_string(e) + ", " +
-                                        (gl ? "true" : "false") + ">");
+                            for (int as : {0, 1})
+                                t.push_back("gemv_kernel<" + std::to_string(m) + ", " + std::to_string(w) + ", " +
+                                            std::to_string(n) + ", " + std::to_string(e) + ", " +
+                                            (gl ? "true" : "false") + (as ? ", true>" : ">"));
         return t;
     }();
     const int mi = mrows == 1 ? 0 : mrows == 2 ? 1 : 2, wi = wk == 4 ? 0 : wk == 8 ? 1 : 2;
     if (ns < 1 || ns > kGemvMaxStages) return "";
-    return table[((((mi * 3 + wi) * kGemvMaxStages + ns - 1) * 2 + (wpe ? 1 : 0)) * 2 + (glu ? 1 : 0))].c_str();
+    return table[(((((mi * 3 + wi) * kGemvMaxStages + ns - 1) * 2 + (wpe ? 1 : 0)) * 2 + (glu ? 1 : 0)) * 2 +
+                  (asym ? 1 : 0))].c_str();
 }
 
 // The decode configurations: rows, K-slices and waves-per-EU hint by M and K.
@@ -1489,11 +1549,7 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
         case Cfg::M64Split: return run_skinny<64, 1, 8, 2, 0>(a, s);
         case Cfg::Gemm64: return run_gemm3<4, 1, 1, 8, 4, 8>(a, s);
         case Cfg::Gemm128W: return run_gemm3<8, 1, 1, 12, 0, 8>(a, s);
-#ifdef GEMM128_CFG
-        default: return run_gemm3<GEMM128_CFG>(a, s);
-#else
         default: return run_gemm3<8, 1, 1, 8, 4, 8>(a, s);
-#endif
     }
 }
 
@@ -1541,6 +1597,59 @@ hipError_t launch_linear_glu(LinearArgs a, hipStream_t s) {
         case Cfg::M64: return run_gemm3<4, 1, 1, 8, 0, 8, true>(a, s);
         case Cfg::Gemm64: return run_gemm3<4, 1, 1, 8, 4, 8, true>(a, s);
         default: return run_gemm3<8, 1, 1, 8, 4, 8, true>(a, s);
+    }
+}
+
+// The asymmetric layout (one segment): up to 4 rows and K up to 12288 the
+// decode kernel (8 K-slices up to K = 3072 at one row and 4096 at two, 16
+// beyond), otherwise the GEMM (32- or 64-row tiles up to 64 rows, the tile
+// model above that).
+namespace {
+enum class Q41 { G1, G1K, G2, G2K, G4, Gemm32, Gemm64r, Gemm64, Gemm128, Gemm128W };
+Q41 pick_q41(const LinearArgs &a) {
+    if (a.M <= 4 && a.KT <= 96) {
+        if (a.M == 1) return a.KT <= 24 ? Q41::G1 : Q41::G1K;
+        if (a.M == 2) return a.KT <= 32 ? Q41::G2 : Q41::G2K;
+        return Q41::G4;
+    }
+    if (a.M <= 32) return Q41::Gemm32;
+    if (a.M <= 64) return Q41::Gemm64r;
+    switch (gemm_shape(a)) {
+        case Cfg::Gemm64: return Q41::Gemm64;
+        case Cfg::Gemm128W: return Q41::Gemm128W;
+        default: return Q41::Gemm128;
+    }
+}
+}  // namespace
+
+const char *linear_q41_config_name(const LinearArgs &a) {
+    const int ns16 = (a.KT + 15) / 16;
+    switch (pick_q41(a)) {
+        case Q41::G1: return gemv_name(1, 8, (a.KT + 7) / 8, 6, false, true);
+        case Q41::G1K: return gemv_name(1, 16, ns16, 0, false, true);
+        case Q41::G2: return gemv_name(2, 8, (a.KT + 7) / 8, 0, false, true);
+        case Q41::G2K: return gemv_name(2, 16, ns16, 0, false, true);
+        case Q41::G4: return gemv_name(4, 16, ns16, 0, false, true);
+        case Q41::Gemm32: return "gemm3_kernel<2, 1, 1, 8, 0, 8, false, true>";
+        case Q41::Gemm64r: return "gemm3_kernel<4, 1, 1, 8, 0, 8, false, true>";
+        case Q41::Gemm64: return "gemm3_kernel<4, 1, 1, 8, 0, 8, false, true>";
+        case Q41::Gemm128W: return "gemm3_kernel<8, 1, 1, 12, 0, 8, false, true>";
+        default: return "gemm3_kernel<8, 1, 1, 8, 0, 8, false, true>";
+    }
+}
+
+hipError_t launch_linear_q41(LinearArgs a, hipStream_t s) {
+    switch (pick_q41(a)) {
+        case Q41::G1: return run_gemv<1, 8, 6, false, 3, true>(a, s);
+        case Q41::G1K: return run_gemv<1, 16, 0, false, 6, true>(a, s);
+        case Q41::G2: return run_gemv<2, 8, 0, false, 4, true>(a, s);
+        case Q41::G2K: return run_gemv<2, 16, 0, false, 6, true>(a, s);
+        case Q41::G4: return run_gemv<4, 16, 0, false, 6, true>(a, s);
+        case Q41::Gemm32: return run_gemm3<2, 1, 1, 8, 0, 8, false, true>(a, s);
+        case Q41::Gemm64r: return run_gemm3<4, 1, 1, 8, 0, 8, false, true>(a, s);
+        case Q41::Gemm64: return run_gemm3<4, 1, 1, 8, 0, 8, false, true>(a, s);
+        case Q41::Gemm128W: return run_gemm3<8, 1, 1, 12, 0, 8, false, true>(a, s);
+        default: return run_gemm3<8, 1, 1, 8, 0, 8, false, true>(a, s);
     }
 }
 

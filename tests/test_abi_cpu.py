@@ -234,3 +234,28 @@ def test_reference_read_validates_first(L):
     assert rr(FAKE, 64, None, None) == NULL
     assert rr(MISALIGNED + 4, 64, FAKE, None) == ALIGN
     assert rr(FAKE, 64, FAKE + 2, None) == ALIGN
+
+
+@pytest.mark.parametrize("n,k", [(4096, 3072), (40, 384), (1, 32), (17, 96)])
+def test_q41_packed_bytes_matches_layout_definition(L, n, k):
+    assert q4.q41_packed_bytes(n, k) == O.q41_packed_bytes(n, k)
+
+
+def test_q41_entry_points_validate_first(L):
+    for fn in (L.q4_1_quantize, L.q4_1_pack, L.q4_1_dequant):
+        assert fn(FAKE, 16, 48, FAKE, None) == SHAPE
+        assert fn(None, 16, 64, FAKE, None) == NULL
+        assert fn(FAKE, 16, 64, MISALIGNED, None) == ALIGN
+    lin = L.q4_1_linear
+    assert lin(FAKE, 1, FAKE, 16, 48, FAKE, None) == SHAPE
+    assert lin(FAKE, -1, FAKE, 16, 64, FAKE, None) == SHAPE
+    assert lin(None, 1, FAKE, 16, 64, FAKE, None) == NULL
+    assert lin(FAKE, 1, FAKE, 16, 64, MISALIGNED, None) == ALIGN
+    assert lin(None, 0, None, 16, 64, None, None) == OK
+    assert L.q4_1_packed_bytes(16, 48) == 0
+    kn = L.q4_1_linear_kernel
+    assert kn(0, 64, 16) == b""
+    assert kn(1, 3072, 4096) == b"gemv_kernel<1, 8, 3, 6, false, true>"
+    assert kn(1, 9216, 3072) == b"gemv_kernel<1, 16, 5, 0, false, true>"
+    assert kn(3, 20480, 64) == b"gemm3_kernel<2, 1, 1, 8, 0, 8, false, true>"   # K past the decode kernel's reach
+    assert kn(40, 3072, 3072) == b"gemm3_kernel<4, 1, 1, 8, 0, 8, false, true>"

@@ -106,6 +106,10 @@ def test_linear_matches_exact_rational_triple_loop(m, n, k):
             assert abs(Fraction(y[i, j]) - exact) <= Fraction(k) * Fraction(2) ** -52 * Fraction(scale)
 
 
+def kt_n_of(k):
+    return -(-k // 128)
+
+
 def test_pack_places_offset_and_keeps_the_q4_0_planes():
     n, k = 20, 160                      # pads to 32 rows and 256 columns
     rng = np.random.default_rng(5)
@@ -116,8 +120,11 @@ def test_pack_places_offset_and_keeps_the_q4_0_planes():
     blocks = O.q41_encode(d, mm, q)
     packed = O.q41_pack(blocks, n, k)
     assert packed.size == O.q41_packed_bytes(n, k) == 32 * (256 // 32) * 20
-    front = O.pack(O.gguf_encode(d, q), n, k)
+    front = O.pack(O.gguf_encode(d, q ^ 8), n, k)          # codes q themselves in the nibble slots
     assert np.array_equal(packed[:front.size], front)
+    # code q of row 5, element 37 (block 1 = kt 0, i = 1; g = 0, j = 5) by the layout rule
+    byte = packed[(0 * kt_n_of(k) + 0) * 1024 + 0 * 256 + 5 * 16 + 1 * 4 + 5 // 2]
+    assert (byte >> 4) == q[5, 37]
     off = packed[front.size:].view(np.float16)
     kt_n = 2
     idx = (1 * kt_n + 1) * 64 + 1 * 4 + 0
