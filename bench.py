@@ -326,7 +326,7 @@ def time_embed(pw, counts, reps, dev, blocks=None):
     return out
 
 
-def time_single(spec, pw, ms, reps, dev):
+def time_single(spec, pw, ms, reps, dev, linear=None, moved_fn=None):
     """One single-segment linear at each M: kernel-own time (armed events) of
     launches that each follow a read of a 512 MiB buffer, so the weights
     stream from HBM rather than from the 256 MB infinity cache (a read, not
@@ -337,6 +337,8 @@ def time_single(spec, pw, ms, reps, dev):
 
     import q4_weight_only_amd as q4
 
+    linear = linear or q4.linear
+    moved_fn = moved_fn or algorithmic_bytes
     flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
     sink = torch.empty((), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -346,7 +348,7 @@ def time_single(spec, pw, ms, reps, dev):
         x = torch.from_numpy(xb.view(np.int16).copy()).to(dev).view(torch.bfloat16)
         y = torch.empty((m, pw.n), dtype=torch.float32, device=dev)
         ys[m] = y
-        q4.linear(x, pw, y)
+        linear(x, pw, y)
         pairs = []
         for _ in range(reps):
             torch.sum(flush, dim=0, out=sink)
@@ -355,13 +357,15 @@ def time_single(spec, pw, ms, reps, dev):
             a.record(stream)
             b.record(stream)
             q4.time_next_launch(a, b)
-            q4.linear(x, pw, y)
+            linear(x, pw, y)
             pairs.append((a, b))
         torch.cuda.synchronize(dev)
         ts = np.array([a.elapsed_time(b) / 1e3 for a, b in pairs])
         t = float(np.median(ts))
-        moved = algorithmic_bytes(spec, m)
-        out[f"M={m}"] = {"kernel": q4.linear_kernel(m, spec.K, spec.Ns), "us": round(t * 1e6, 2),
+        moved = moved_fn(spec, m)
+        kname = (q4.q41_linear_kernel(m, spec.K, spec.Ns[0]) if linear is q4.q41_linear
+                 else q4.linear_kernel(m, spec.K, spec.Ns))
+        out[f"M={m}"] = {"kernel": kname, "us": round(t * 1e6, 2),
                          "p10_us": round(float(np.percentile(ts, 10)) * 1e6, 2),
                          "p90_us": round(float(np.percentile(ts, 90)) * 1e6, 2),
                          "GBs": round(moved / t / 1e9, 1), "frac_of_8TBs": round(moved / t / 1e9 / HBM_PEAK_GBS, 4),
@@ -794,6 +798,35 @@ def main():
                                   cpu_oracle_rate(jobs, 1, "GFLOP/s", "M=1505 through the first 512 rows of the "
                                                                          "adapter 5120->3072"))
             log(f"workload {key}: {wl[key]}")
+
+    # ---- the asymmetric variant (w = q d + m per block): the decoder shapes, each
+    # matrix alone, at M = 1 and 2048 (layer-0 weights, quantized on the device)
+    if not args.no_others:
+        from q4_weight_only_amd.inputs import LinearSpec
+
+        rec, checks = {}, []
+        for spec in specs[:4]:
+            for si, n in enumerate(spec.Ns):
+                one = LinearSpec(f"{spec.name}.{si}", spec.K, (n,), [spec.w_tags[si]], spec.x_tags)
+                w = one.weight(0)
+                pw = q4.q41_pack(q4.q41_quantize(torch.from_numpy(w).to(dev)), n, spec.K)
+                res, ys = time_single(one, pw, (1, 2048), 10, dev, linear=q4.q41_linear,
+                                      moved_fn=lambda sp, m: sp.Ns[0] * sp.K // 32 * 20 + m * sp.K * 2 + m * sp.Ns[0] * 4)
+                for mk, r in res.items():
+                    rec[f"{spec.name.split('.', 1)[1]}[{si}] {spec.K}->{n} {mk}"] = r
+                rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(si).choice(n, 46, replace=False)]))
+                blocks = O.q41_quantize(np.ascontiguousarray(w[rows]))
+                for m in (1, 2048):
+                    ref, bound = O.q41_linear_with_bound(one.activations(m), blocks, len(rows), spec.K)
+                    yv = ys[m][:, rows].cpu().numpy().astype(np.float64)
+                    checks.append((float(np.max(np.abs(yv - ref) / bound)),
+                                   float(np.dot(yv.ravel(), ref.ravel()) / (np.linalg.norm(yv) * np.linalg.norm(ref)))))
+                del pw, ys, w
+        out["variant_q41"] = {
+            "workload": "asymmetric 4-bit blocks (w = q d + m, 20 bytes per 32 weights): the decoder's seven weight "
+                        "matrices of layer 0, one launch each, from HBM, at M=1 (GB/s) and M=2048 (TFLOP/s)",
+            **rec, "parity": parity_record(checks)}
+        log(f"variant q41: {out['variant_q41']}")
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
