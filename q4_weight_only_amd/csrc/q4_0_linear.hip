@@ -125,7 +125,15 @@ __device__ __forceinline__ floatx4 mfma_block(const bf16x8 &a, const bf16x8 &b) 
 
 // silu(g) = g / (1 + e^-g) in fp32 (expf overflows to +inf for g below
 // about -88, which gives -0: the true value is below 1e-36 there).
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+// silu(g) = g / (1 + e^-g), as g * rcp(1 + 2^(-g log2 e)) with the hardware
+// exp2 and reciprocal (about 1 ulp each).  The rounding of -g log2 e adds a
+// relative error of at most |g| 2^-24 log2 e ln 2, under 6e-6 while e^-g is
+// finite (g > -88).  Below that e^-g overflows and the result is -0 (the
+// exact value is under 1e-36 in magnitude); g = -inf gives NaN, as the
+// quotient does.
+__device__ __forceinline__ float silu_f32(float g) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504f));
+}
 
 // Epilogue store of one output: fp32, or for a gated launch that asks for it
 // bf16 rounded to nearest even (the y pointer then addresses bf16 elements).
@@ -706,10 +714,16 @@ __device__ __forceinline__ int a_tile_offset(int m, int c) { return (m * 16 + (c
 // step kt computes (the x tile is double-buffered in LDS either way).  Each
 // weight tile is read by one workgroup per 64 rows of x, so the weight loads
 // are nontemporal.
-template <int MT, int NT, int WM, int WN, int WPE, int PB>
+//
+// GLU: as in gemm3_kernel, the first WN / 2 waves of a workgroup row run
+// gate rows and the last WN / 2 the same rows of up, each exactly as a plain
+// launch would, and the up waves hand their results to the gate waves
+// through LDS for the silu(gate) * up epilogue.
+template <int MT, int NT, int WM, int WN, int WPE, int PB, bool GLU = false>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
 void gemm_kernel(const LinearArgs a) {
     static_assert(PB >= 2, "at least one step of weights in flight");
+    static_assert(!GLU || (WN % 2 == 0 && (WN / 2) * NT <= 8), "gate / up waves and their LDS hand-off");
     using C = GemmCfg<MT, NT, WM, WN>;
     constexpr int BM = C::BM, NPT = C::kAPerThread;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * 256];
@@ -720,9 +734,13 @@ void gemm_kernel(const LinearArgs a) {
     const int wm = wave / WN, wn = wave % WN;
     const int nl = lane & 15, g = lane >> 4;
 
-    const int s = find_segment(a, blockIdx.x);
+    constexpr int WNO = GLU ? WN / 2 : WN;   // waves per workgroup row with distinct output rows
+    const bool up_wave = GLU && wn >= WNO;
+    const int wno = GLU ? wn % WNO : wn;
+    const int s = GLU ? 0 : find_segment(a, blockIdx.x);
     const Segment sg = a.seg[s];
-    const int rt_base = (static_cast<int>(blockIdx.x) - sg.tile_begin) * (NT * WN) + wn * NT;
+    const Segment &src = up_wave ? a.seg[1] : sg;   // the matrix this wave streams
+    const int rt_base = (static_cast<int>(blockIdx.x) - sg.tile_begin) * (NT * WNO) + wno * NT;
     const int m0 = blockIdx.y * BM;
     const int KT = a.KT;
     const int nblk = a.K / kQK;
@@ -756,10 +774,10 @@ void gemm_kernel(const LinearArgs a) {
     const uint16_t *sc_base[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const int rt = rt_base + nt < sg.RT ? rt_base + nt : sg.RT - 1;
+        const int rt = rt_base + nt < src.RT ? rt_base + nt : src.RT - 1;
         const int64_t T0 = static_cast<int64_t>(rt) * KT;
-        nib_base[nt] = sg.nib + T0 * kTileNibBytes + lane * 16;
-        sc_base[nt] = sg.scales + T0 * kTileScales + nl * 4;
+        nib_base[nt] = src.nib + T0 * kTileNibBytes + lane * 16;
+        sc_base[nt] = src.scales + T0 * kTileScales + nl * 4;
     }
     struct BStage {
         u32x4 nib[NT];
@@ -846,6 +864,23 @@ void gemm_kernel(const LinearArgs a) {
         if (done) break;
     }
 
+    // gated: once every wave is past its last step's x reads, the up waves
+    // leave their results in the x buffers for the matching gate wave
+    float *xch = reinterpret_cast<float *>(&lds_a[0][0]) + (wm * WNO + wno) * (MT * NT * 4 * 64);
+    if constexpr (GLU) {
+        __syncthreads();
+        if (up_wave) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) xch[((mt * NT + nt) * 4 + r) * 64 + lane] = acc[mt][nt][r];
+        }
+        __syncthreads();
+        if (up_wave) return;
+    }
+
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int rt = rt_base + nt;
@@ -856,7 +891,12 @@ void gemm_kernel(const LinearArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + (wm * MT + mt) * 16 + 4 * g + r;
-                if (m < a.M) sg.y[static_cast<int64_t>(m) * sg.N + n] = acc[mt][nt][r] * 16.0f;
+                if (m >= a.M) continue;
+                if constexpr (GLU)
+                    store_out(a, sg, static_cast<int64_t>(m) * sg.N + n,
+                              silu_f32(acc[mt][nt][r] * 16.0f) * (xch[((mt * NT + nt) * 4 + r) * 64 + lane] * 16.0f));
+                else
+                    sg.y[static_cast<int64_t>(m) * sg.N + n] = acc[mt][nt][r] * 16.0f;
             }
     }
 }
@@ -1316,12 +1356,12 @@ hipError_t run_gemv(LinearArgs a, hipStream_t s) {
     return hipErrorInvalidValue;   // the dispatch never asks for more than NSMAX stages
 }
 
-template <int MT, int NT, int WM, int WN, int WPE = 0, int PB = 2>
+template <int MT, int NT, int WM, int WN, int WPE = 0, int PB = 2, bool GLU = false>
 hipError_t run_gemm(LinearArgs a, hipStream_t s) {
     using C = GemmCfg<MT, NT, WM, WN>;
-    const int tiles = assign_tiles<false>(a, NT * WN);
+    const int tiles = assign_tiles<GLU>(a, NT * (GLU ? WN / 2 : WN));
     const int mtiles = (a.M + C::BM - 1) / C::BM;
-    return launch_kernel(gemm_kernel<MT, NT, WM, WN, WPE, PB>, dim3(tiles, mtiles), dim3(C::kThreads), 0, s, a);
+    return launch_kernel(gemm_kernel<MT, NT, WM, WN, WPE, PB, GLU>, dim3(tiles, mtiles), dim3(C::kThreads), 0, s, a);
 }
 
 template <int MT, int NT, int WM, int WN, int WPE = 0, int GM = 8, bool GLU = false, bool ASYM = false>
@@ -1555,8 +1595,8 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
 
 // The gated (SwiGLU) launch: the plain configurations with the gate and up
 // rows of a tile on separate waves (skinny: 2 WK waves, at most 8 K-slices
-// so a workgroup stays within 1024 threads; gemm3: WN / 2 gate and WN / 2 up
-// waves), so every wave runs the plain arithmetic.
+// so a workgroup stays within 1024 threads; gemm and gemm3: WN / 2 gate and
+// WN / 2 up waves), so every wave runs the plain arithmetic.
 // The gated launch's decode configurations are the plain ones (its
 // workgroups cover 8 gate and 8 up rows: the plain wave count per workgroup).
 GemvCfg gemv_glu_cfg(Cfg c) { return gemv_cfg(c); }
@@ -1573,8 +1613,8 @@ const char *linear_glu_config_name(int64_t M, int64_t K) {
         case Cfg::M4Long: return skinny_name(M, K, 4, "skinny_kernel<4, 1, 8, 3, true, 0, true>", "skinny_kernel<4, 1, 8, 3, false, 0, true>");
         case Cfg::M16: return skinny_name(M, K, 16, "skinny_kernel<16, 1, 4, 2, true, 0, true>", "skinny_kernel<16, 1, 4, 2, false, 0, true>");
         case Cfg::M16Long: return skinny_name(M, K, 16, "skinny_kernel<16, 1, 8, 3, true, 0, true>", "skinny_kernel<16, 1, 8, 3, false, 0, true>");
-        case Cfg::M32: return "gemm3_kernel<2, 1, 1, 8, 0, 8, true>";
-        case Cfg::M64: return "gemm3_kernel<4, 1, 1, 8, 0, 8, true>";
+        case Cfg::M32: return "gemm_kernel<2, 1, 1, 8, 0, 2, true>";
+        case Cfg::M64: return "gemm_kernel<4, 1, 1, 8, 0, 3, true>";
         case Cfg::Gemm64: return "gemm3_kernel<4, 1, 1, 8, 4, 8, true>";
         default: return "gemm3_kernel<8, 1, 1, 8, 4, 8, true>";
     }
@@ -1593,8 +1633,8 @@ hipError_t launch_linear_glu(LinearArgs a, hipStream_t s) {
         case Cfg::M4Long: return run_skinny<4, 1, 8, 3, 0, true>(a, s);
         case Cfg::M16: return run_skinny<16, 1, 4, 2, 0, true>(a, s);
         case Cfg::M16Long: return run_skinny<16, 1, 8, 3, 0, true>(a, s);
-        case Cfg::M32: return run_gemm3<2, 1, 1, 8, 0, 8, true>(a, s);
-        case Cfg::M64: return run_gemm3<4, 1, 1, 8, 0, 8, true>(a, s);
+        case Cfg::M32: return run_gemm<2, 1, 1, 8, 0, 2, true>(a, s);
+        case Cfg::M64: return run_gemm<4, 1, 1, 8, 0, 3, true>(a, s);
         case Cfg::Gemm64: return run_gemm3<4, 1, 1, 8, 4, 8, true>(a, s);
         default: return run_gemm3<8, 1, 1, 8, 4, 8, true>(a, s);
     }

@@ -149,6 +149,8 @@ def test_linear_kernel_names(L):
     assert L.q4_0_linear_swiglu_kernel(1, 3072) == b"gemv_kernel<1, 8, 3, 6, true>"
     assert L.q4_0_linear_swiglu_kernel(2, 4096) == b"gemv_kernel<2, 8, 4, 0, true>"
     assert L.q4_0_linear_swiglu_kernel(1, 4096) == b"gemv_kernel<1, 16, 2, 0, true>"
+    assert L.q4_0_linear_swiglu_kernel(32, 3072) == b"gemm_kernel<2, 1, 1, 8, 0, 2, true>"   # 17-32 rows
+    assert L.q4_0_linear_swiglu_kernel(64, 3072) == b"gemm_kernel<4, 1, 1, 8, 0, 3, true>"   # 33-64 rows
     import torch
     if torch.cuda.is_available() and torch.cuda.get_device_properties(0).multi_processor_count != 256:
         return                                          # the tile counts below assume 256 CUs
