@@ -248,12 +248,15 @@ const char *q4_0_linear_kernel(int64_t M, int64_t K, const int64_t *N, int nseg)
  * Inputs must be finite; bit-for-bit reproducible.
  * q4_1_pack / q4_1_dequant: as their Q4_0 counterparts (w = q * d + m rounded
  * once to fp32).
- * q4_1_linear: y[M, N] (fp32) = x[M, K] (bf16) times W^T.  Each block's
- * sum of x * q and sum of x are formed by MFMAs and added as d * (sum x q) +
- * m * (sum x) in fp32, so y is within 1e-3 * sum_k |x_k| (|q_k d| + |m|)
- * + 1e-6 of the exact result for finite inputs (both terms' magnitudes:
- * q d and m may cancel in w).  Deterministic.  Sizes, validation and errors
- * as for q4_0_linear.
+ * q4_1_linear: y[M, N] (fp32) = x[M, K] (bf16) times W^T, computed as
+ * sum over blocks of d * (sum x q) + m * (sum x): each block's sum of x * q
+ * and sum of x are formed by MFMAs; up to 4 rows each block then adds both
+ * terms in fp32, above 4 rows the offsets' share of each run of 8 blocks is
+ * one more MFMA over bf16 hi / lo parts of m (exact) and of the sums of x
+ * (within 2^-16).  y is within 1e-3 * sum_k |x_k| (|q_k d| + |m|) + 1e-6 of
+ * the exact result for finite inputs (both terms' magnitudes: q d and m may
+ * cancel in w).  Deterministic; above 4 rows an output's bits do not depend
+ * on M.  Sizes, validation and errors as for q4_0_linear.
  */
 size_t q4_1_packed_bytes(int64_t N, int64_t K);   /* 0 if N or K is invalid */
 q4_status q4_1_quantize(const float *w, int64_t N, int64_t K, void *blocks, void *stream);

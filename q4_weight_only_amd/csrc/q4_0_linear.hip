@@ -123,8 +123,17 @@ __device__ __forceinline__ floatx4 mfma_block(const bf16x8 &a, const bf16x8 &b) 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, (floatx4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 }
 
-// silu(g) = g / (1 + e^-g) in fp32 (expf overflows to +inf for g below
-// about -88, which gives -0: the true value is below 1e-36 there).
+// An fp32 value as two bf16 (bit patterns in the low 16 bits): hi is v with
+// its low 16 bits cleared, lo the remainder v - hi (exact in fp32) rounded
+// to nearest even, so hi + lo is v within 2^-16 |v|, and exactly v when v
+// has at most 16 significant bits (an fp16 value has 11).
+__device__ __forceinline__ void split_bf16(float v, uint32_t &hi, uint32_t &lo) {
+    const uint32_t vb = __builtin_bit_cast(uint32_t, v);
+    hi = vb >> 16;
+    const float r = v - __builtin_bit_cast(float, vb & 0xFFFF0000u);
+    lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(r));
+}
+
 // silu(g) = g / (1 + e^-g), as g * rcp(1 + 2^(-g log2 e)) with the hardware
 // exp2 and reciprocal (about 1 ulp each).  The rounding of -g log2 e adds a
 // relative error of at most |g| 2^-24 log2 e ln 2, under 6e-6 while e^-g is
@@ -908,7 +917,10 @@ void gemm_kernel(const LinearArgs a) {
 // each group of MFMA results is issued after the next group's MFMAs, so the
 // FMAs never wait on a result still in flight.  Work tiles are mapped to
 // workgroups so that each of the 8 XCDs owns a contiguous range of them, in
-// an order where GM consecutive tiles share one weight tile.
+// an order where GM consecutive tiles share one weight tile.  128-row tiles
+// take GM = 4: an XCD's resident workgroups then cover 4 x tiles (3 MiB of x
+// at K = 3072, within its 4 MiB L2) and 16 weight tiles; at M = 2048 that
+// read 31-35% fewer bytes from beyond L2 than groups of 8, in the same time.
 template <int MT, int NT, int WM, int WN>
 struct Gemm3Cfg {
     static constexpr int BM = 16 * MT * WM;
@@ -934,16 +946,29 @@ struct Gemm3Cfg {
 // plain launch would; the up waves hand their results to the gate waves
 // through LDS for the silu(gate) * up epilogue.
 //
-// ASYM: the asymmetric layout, as in gemv_kernel: codes decoded as q, the
-// block sums of x from an MFMA against ones (once per m-tile and block), and
-// d * D + m * S added per block.
+// ASYM: the asymmetric layout (w = q d + m).  The codes are decoded as q and
+// each block's product D is rescaled by d as in the symmetric kernel; the
+// offsets' share, sum over blocks b of m[n, b] S[row, b] with S the block
+// sums of x, is itself a small product, taken on the matrix cores once per
+// 8 blocks.  Per 128-k step, wave w < MT computes S for m-tile w (four
+// MFMAs against its x fragments, block i with A rows 4i .. 4i + 3 set to
+// ones, leave S[row r, block g] in lane 16 g + r) and stores S split into
+// bf16 hi + lo in LDS; per 8 blocks every wave
+// builds MFMA A fragments from them and multiplies by its rows' offsets,
+// split the same way (exactly: fp16 has 11 significant bits), accumulating
+// into acc: k = 4 b + t pairs (S_hi, m_hi), (S_hi, m_lo), (S_lo, m_hi),
+// (S_lo, m_lo).
 template <int MT, int NT, int WM, int WN, int WPE, int GM, bool GLU, bool ASYM = false>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
 void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
     static_assert(!(GLU && ASYM), "no gated launch of the asymmetric layout");
+    static_assert(!ASYM || (WM == 1 && WN >= MT), "asymmetric: one wave per m-tile computes its block sums");
     using C = Gemm3Cfg<MT, NT, WM, WN>;
     constexpr int BM = C::BM, NPT = C::kAPerThread;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * 256];
+    // asymmetric: S of two 8-block windows, the one being read and the one
+    // being written, as (hi, lo) bf16 pairs [m-tile][row][block]
+    __shared__ __attribute__((aligned(16))) uint32_t lds_s[ASYM ? 2 : 1][ASYM ? MT * 16 * 8 : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1025,15 +1050,12 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
     struct BStage {
         u32x4 nib[NT];
         u32x2 sc[NT];
-        u32x2 off[ASYM ? NT : 1];
     };
     auto load_b = [&](BStage &S, int kt) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             S.nib[nt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(nib_rsrc[nt], nib_lane, kt * kTileNibBytes, 0));
             S.sc[nt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(sc_rsrc[nt], sc_lane, kt * kTileScales * 2, 0));
-            if constexpr (ASYM)
-                S.off[nt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(off_rsrc[nt], sc_lane, kt * kTileScales * 2, 0));
         }
     };
 
@@ -1044,6 +1066,20 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
     const int a_row0 = (wm * MT) * 16 + nl;   // LDS row of m-tile 0 for this lane; m-tile mt adds 16 mt
+    // asymmetric: this step's block sums (of m-tile wave % MT), and per
+    // n-tile the two offsets (an fp16 pair) of this lane's blocks 2g, 2g + 1
+    // of an 8-block window: row nl of super-tile 2 win + g / 2, blocks
+    // 2 (g & 1), + 1.  The whole offset is in the per-lane (range-checked)
+    // part, so a super-tile past K reads zeros.
+    floatx4 ssum = (floatx4){0.f, 0.f, 0.f, 0.f};
+    uint32_t mpair[NT];
+    const int m_lane = nl * 8 + (g & 1) * 4 + (g >> 1) * kTileScales * 2;
+    auto load_offsets = [&](int win) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            mpair[nt] = __builtin_amdgcn_raw_buffer_load_b32(off_rsrc[nt], m_lane + 2 * win * kTileScales * 2, 0, 0);
+    };
+
     auto compute_block = [&](int buf, const BStage &S, int i) {
         const uint8_t *tile = lds_a[buf];
         const int sw = ((4 * i + g) ^ nl) * 16;   // swizzled chunk of block i (row & 15 == nl)
@@ -1052,27 +1088,18 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
         for (int mt = 0; mt < MT; ++mt)
             A[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(tile + (a_row0 + 16 * mt) * 256 + sw));
         if constexpr (ASYM) {
-            floatx4 Sx[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) Sx[mt] = mfma_block(A[mt], bf16_ones());
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const bf16x8 B = decode_piece_u(piece_of(S.nib[nt], i));
-                const float d = scale_of(S.sc[nt], i), m = scale_of(S.off[nt], i);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const floatx4 D = mfma_block(A[mt], B);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        acc[mt][nt][r] = fmaf(d, D[r], acc[mt][nt][r]);
-                        acc[mt][nt][r] = fmaf(m, Sx[mt][r], acc[mt][nt][r]);
-                    }
-                }
-            }
-        } else
+            // block sums of x for m-tile wave % MT (waves past MT repeat
+            // one, without a branch): A rows 4i .. 4i + 3 are ones, so after
+            // the step's four blocks lane 16 g + r holds S[row r, block g]
+            const bf16x8 X = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4 *>(tile + ((wave % MT) * 16 + nl) * 256 + sw));
+            const uint32_t ones = (nl >> 2) == i ? 0x3F803F80u : 0u;   // two bf16 1.0
+            ssum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, (u32x4){ones, ones, ones, ones}),
+                                                           X, i == 0 ? (floatx4){0.f, 0.f, 0.f, 0.f} : ssum, 0, 0, 0);
+        }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const bf16x8 B = decode_piece(piece_of(S.nib[nt], i));
+            const bf16x8 B = ASYM ? decode_piece_u(piece_of(S.nib[nt], i)) : decode_piece(piece_of(S.nib[nt], i));
             const float d = scale_of(S.sc[nt], i);
             // each MFMA's rescale is issued after the next MFMA, so the FMAs
             // never wait on a result still in the matrix pipe
@@ -1107,6 +1134,43 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
     }
     __syncthreads();
 
+    // asymmetric: the offsets' share of 8-block window `win` (steps 2 win and
+    // 2 win + 1) into acc.  `half`: the window's second step lies past K, and
+    // lanes g >= 2 (its blocks) add zeros.
+    auto offset_term = [&](int win, bool half) {
+        const bool zero = half && g >= 2;
+        bf16x8 MB[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            uint32_t h0, l0, h1, l1;
+            split_bf16(half_bits_to_float(mpair[nt] & 0xFFFFu), h0, l0);
+            split_bf16(half_bits_to_float(mpair[nt] >> 16), h1, l1);
+            const uint32_t w0 = zero ? 0u : h0 | (l0 << 16), w1 = zero ? 0u : h1 | (l1 << 16);
+            MB[nt] = __builtin_bit_cast(bf16x8, (u32x4){w0, w0, w1, w1});
+        }
+        const uint32_t *sb = lds_s[win & 1] + nl * 8 + 2 * g;   // row nl, blocks 2g, 2g + 1
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const u32x2 p = zero ? (u32x2){0u, 0u} : *reinterpret_cast<const u32x2 *>(sb + mt * 128);
+            // (hi, hi), (lo, lo) of each block: byte selects of its pair
+            const u32x4 sa = (u32x4){__builtin_amdgcn_perm(p.x, p.x, 0x01000100u), __builtin_amdgcn_perm(p.x, p.x, 0x03020302u),
+                                     __builtin_amdgcn_perm(p.y, p.y, 0x01000100u), __builtin_amdgcn_perm(p.y, p.y, 0x03020302u)};
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, sa), MB[nt],
+                                                                      acc[mt][nt], 0, 0, 0);
+        }
+    };
+    // asymmetric, after the blocks of step kt (parity cur): lane (r, g)
+    // stores S of row r, block g of the step, for m-tile wave % MT (waves
+    // past MT store the same bytes as wave % MT).  No store here depends on
+    // the lane: as a branch it cost some 70 more registers.
+    auto window_part = [&](int kt, int cur) {
+        uint32_t h, l;
+        split_bf16(ssum[0], h, l);
+        lds_s[(kt >> 1) & 1][(wave % MT) * 128 + nl * 8 + 4 * cur + g] = h | (l << 16);
+    };
+
     // One 128-k step with no branches: the loads for step kt + 1 are clamped
     // to the last step (the extra loads and stores of the final step go to
     // the buffer nobody reads any more).  Loads complete in issue order for
@@ -1120,6 +1184,10 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
         load_part(R0, kn, 0);
         load_part(R1, kn, 1);
         load_b(bn, kn);
+        if constexpr (ASYM) {
+            if (cur == 0 && kt > 0) offset_term((kt >> 1) - 1, false);   // the window that ended
+            if (cur == 0) load_offsets(kt >> 1);                        // the window that starts
+        }
         compute_block(cur, bc, 0);
         store_part(R0, cur ^ 1, 0);
         load_part(R0, kn, 2);
@@ -1130,6 +1198,7 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
         store_part(R0, cur ^ 1, 2);
         compute_block(cur, bc, 3);
         store_part(R1, cur ^ 1, 3);
+        if constexpr (ASYM) window_part(kt, cur);
         __syncthreads();
     };
     for (int kt = 0;;) {
@@ -1138,6 +1207,7 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
         step(kt, 1, b1, b0);
         if (++kt == KT) break;
     }
+    if constexpr (ASYM) offset_term((KT - 1) >> 1, (KT & 1) != 0);   // the last window (one step if KT is odd)
 
     // gated: the up waves leave their results in LDS (the x buffers are free
     // once the last step's barrier has passed) for the matching gate wave
@@ -1563,8 +1633,8 @@ const char *linear_config_name(const LinearArgs &a) {
         case Cfg::M64: return "gemm_kernel<4, 1, 1, 8, 0, 3>";
         case Cfg::M64Split: return skinny_name(M, K, 64, "skinny_kernel<64, 1, 8, 2, true, 0, false>", "skinny_kernel<64, 1, 8, 2, false, 0, false>");
         case Cfg::Gemm64: return "gemm3_kernel<4, 1, 1, 8, 4, 8, false>";
-        case Cfg::Gemm128W: return "gemm3_kernel<8, 1, 1, 12, 0, 8, false>";
-        default: return "gemm3_kernel<8, 1, 1, 8, 4, 8, false>";
+        case Cfg::Gemm128W: return "gemm3_kernel<8, 1, 1, 12, 0, 4, false>";
+        default: return "gemm3_kernel<8, 1, 1, 8, 4, 4, false>";
     }
 }
 
@@ -1588,8 +1658,8 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
         case Cfg::M64: return run_gemm<4, 1, 1, 8, 0, 3>(a, s);
         case Cfg::M64Split: return run_skinny<64, 1, 8, 2, 0>(a, s);
         case Cfg::Gemm64: return run_gemm3<4, 1, 1, 8, 4, 8>(a, s);
-        case Cfg::Gemm128W: return run_gemm3<8, 1, 1, 12, 0, 8>(a, s);
-        default: return run_gemm3<8, 1, 1, 8, 4, 8>(a, s);
+        case Cfg::Gemm128W: return run_gemm3<8, 1, 1, 12, 0, 4>(a, s);
+        default: return run_gemm3<8, 1, 1, 8, 4, 4>(a, s);
     }
 }
 
@@ -1616,7 +1686,7 @@ const char *linear_glu_config_name(int64_t M, int64_t K) {
         case Cfg::M32: return "gemm_kernel<2, 1, 1, 8, 0, 2, true>";
         case Cfg::M64: return "gemm_kernel<4, 1, 1, 8, 0, 3, true>";
         case Cfg::Gemm64: return "gemm3_kernel<4, 1, 1, 8, 4, 8, true>";
-        default: return "gemm3_kernel<8, 1, 1, 8, 4, 8, true>";
+        default: return "gemm3_kernel<8, 1, 1, 8, 4, 4, true>";
     }
 }
 
@@ -1636,7 +1706,7 @@ hipError_t launch_linear_glu(LinearArgs a, hipStream_t s) {
         case Cfg::M32: return run_gemm<2, 1, 1, 8, 0, 2, true>(a, s);
         case Cfg::M64: return run_gemm<4, 1, 1, 8, 0, 3, true>(a, s);
         case Cfg::Gemm64: return run_gemm3<4, 1, 1, 8, 4, 8, true>(a, s);
-        default: return run_gemm3<8, 1, 1, 8, 4, 8, true>(a, s);
+        default: return run_gemm3<8, 1, 1, 8, 4, 4, true>(a, s);
     }
 }
 

@@ -98,3 +98,22 @@ def test_deterministic(m):
     a = q4.q41_linear(x, pw).cpu().numpy()
     b = q4.q41_linear(x, pw).cpu().numpy()
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_gemm_tile_shapes_agree_bitwise():
+    """Above 4 rows every tile shape of the GEMM adds an output's block
+    results, and the offsets' share of each 8-block window, in the same
+    order, so a row computed in a 32-, 64- or 128-row tile (128 or 192
+    columns wide) has the same bits.  K = 1280 has five windows, K = 1152 an
+    odd step count (its last window has one step)."""
+    for k, n in ((1280, 3072), (1152, 4096)):
+        pw, _ = _weights(n, k, 6)
+        x = to_dev_x(inputs.activations_bf16((2048, k), seed=6, tags=(41, k)))
+        full = q4.q41_linear(x, pw)
+        names = {q4.q41_linear_kernel(2048, k, n)}
+        for m in (32, 64, 300):
+            say("q41 tiles", k, m, q4.q41_linear_kernel(m, k, n))
+            names.add(q4.q41_linear_kernel(m, k, n))
+            part = q4.q41_linear(x[:m], pw)
+            assert torch.equal(part.view(torch.int32), full[:m].view(torch.int32)), f"K={k} M={m}"
+        assert len(names) >= 3, names

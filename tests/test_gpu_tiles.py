@@ -73,7 +73,7 @@ def test_tile_shape_names():
     cus = torch.cuda.get_device_properties(DEV).multi_processor_count
     if cus != 256:
         pytest.skip(f"tile counts here assume 256 compute units, the device has {cus}")
-    assert q4.linear_kernel(2048, 4096, 3072) == "gemm3_kernel<8, 1, 1, 12, 0, 8, false>"
-    assert q4.linear_kernel(2048, 3072, (3072, 3072, 3072)) == "gemm3_kernel<8, 1, 1, 8, 4, 8, false>"
-    assert q4.linear_kernel(2048, 3072, (9216, 9216)) == "gemm3_kernel<8, 1, 1, 8, 4, 8, false>"
+    assert q4.linear_kernel(2048, 4096, 3072) == "gemm3_kernel<8, 1, 1, 12, 0, 4, false>"
+    assert q4.linear_kernel(2048, 3072, (3072, 3072, 3072)) == "gemm3_kernel<8, 1, 1, 8, 4, 4, false>"
+    assert q4.linear_kernel(2048, 3072, (9216, 9216)) == "gemm3_kernel<8, 1, 1, 8, 4, 4, false>"
     assert q4.linear_kernel(300, 3072, 3072) == "gemm3_kernel<4, 1, 1, 8, 4, 8, false>"
