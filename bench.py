@@ -23,11 +23,17 @@ Printed (one JSON line):
                names, parity of the timed outputs against the oracle on sampled
                weight rows (max |err|/bound, cosine) and the oracle's own rate on
                the host cores over a stated sample
+  prefill.arithmetic_ceiling  the GEMM's inner-loop arithmetic alone (MFMAs;
+               + the exact rescale; + the decode), the rate the exact method
+               allows apart from memory
   decode_floor the same 104-launch step with a plain read of the same weight
                bytes in each launch, and with 104 empty launches: what a step
                of this launch structure costs without the layer's arithmetic
   swiglu       the fused gate/up + SwiGLU launch next to the unfused gate/up
-               launch it replaces, at M = 1, 2 and 2048 (kernel-own times)
+               launch it replaces, at M = 1, 2 and 2048 (kernel-own times);
+               and, timed by stream events around the calls, the fused launch
+               next to the unfused launch followed by torch's silu(g) * u (the
+               whole unfused step)
   embed        Q4 embedding lookups of 32, 2048 and 16384 random ids from the
                131072 x 3072 table, packed and as GGUF blocks (key gguf)
   cpu_baseline the oracle (dequantize + fp64 matmul) over the whole decode step
@@ -231,7 +237,10 @@ def time_swiglu(prepared, ms, reps, dev):
     unfused gate/up launch it replaces, over the decode workload's gate/up
     weights.  Each kind of launch walks all layers' weight pairs in turn, so
     25 other pairs (800 MB) stream through between two uses of one pair and
-    every launch reads its weights from HBM, not from the infinity cache."""
+    every launch reads its weights from HBM, not from the infinity cache.
+    Two more kinds are timed by events recorded on the stream around the
+    calls (launch gaps included): the fused launch, and the unfused launch
+    followed by torch's silu(g) * u into h (the unfused step in full)."""
     import numpy as np
     import torch
 
@@ -248,21 +257,31 @@ def time_swiglu(prepared, ms, reps, dev):
         h = torch.empty((m, n), dtype=torch.float32, device=dev)
         h16 = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for _ in range(2)]
-        pairs = {"fused": [], "fused_bf16": [], "unfused": []}
+        kinds = ("fused", "fused_bf16", "unfused", "fused_stream", "unfused_silu_stream")
+        pairs = {kind: [] for kind in kinds}
         for r in range(reps + 1):
-            for kind in ("fused", "fused_bf16", "unfused"):
+            for kind in kinds:
                 for _, pws in gate_up:
                     a = torch.cuda.Event(enable_timing=True)
                     b = torch.cuda.Event(enable_timing=True)
-                    a.record(stream)
-                    b.record(stream)
-                    q4.time_next_launch(a, b)
-                    if kind == "fused":
-                        q4.linear_swiglu(x, pws[0], pws[1], h)
-                    elif kind == "fused_bf16":
-                        q4.linear_swiglu(x, pws[0], pws[1], h16, dtype=torch.bfloat16)
+                    if kind.endswith("_stream"):
+                        a.record(stream)
+                        if kind == "fused_stream":
+                            q4.linear_swiglu(x, pws[0], pws[1], h)
+                        else:
+                            q4.linear_multi(x, pws, ys)
+                            torch.mul(torch.nn.functional.silu(ys[0]), ys[1], out=h)
+                        b.record(stream)
                     else:
-                        q4.linear_multi(x, pws, ys)
+                        a.record(stream)
+                        b.record(stream)
+                        q4.time_next_launch(a, b)
+                        if kind == "fused":
+                            q4.linear_swiglu(x, pws[0], pws[1], h)
+                        elif kind == "fused_bf16":
+                            q4.linear_swiglu(x, pws[0], pws[1], h16, dtype=torch.bfloat16)
+                        else:
+                            q4.linear_multi(x, pws, ys)
                     if r > 0:              # the first pass warms up
                         pairs[kind].append((a, b))
         torch.cuda.synchronize(dev)
@@ -276,6 +295,8 @@ def time_swiglu(prepared, ms, reps, dev):
             "fused_us": round(t["fused"] * 1e6, 2),
             "fused_bf16_out_us": round(t["fused_bf16"] * 1e6, 2),
             "unfused_us": round(t["unfused"] * 1e6, 2),
+            "fused_stream_us": round(t["fused_stream"] * 1e6, 2),
+            "unfused_with_silu_mul_stream_us": round(t["unfused_silu_stream"] * 1e6, 2),
             "fused_GBs": round(fused_bytes / t["fused"] / 1e9, 1),
             "unfused_GBs": round(unfused_bytes / t["unfused"] / 1e9, 1),
             "fused_TFLOPs": round(fl / t["fused"] / 1e12, 2),
@@ -490,6 +511,36 @@ def cpu_oracle_rate(jobs, runs, unit, sample):
 
 
 # ---------------------------------------------------------- decode floor
+def time_ceiling(dev, iterations=2000, reps=5):
+    """The prefill GEMM's arithmetic alone (q4_0_reference_mfma): kernel-own
+    TFLOP/s of the MFMAs, of the MFMAs with the exact fp32 rescale, and of
+    both with the nibble decode, median of `reps` launches each."""
+    import numpy as np
+    import torch
+
+    import q4_weight_only_amd as q4
+
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for mode, key in ((0, "mfma_only"), (1, "mfma_rescale"), (2, "mfma_rescale_decode")):
+        q4.reference_mfma(mode, 10, dev)
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            b.record(stream)
+            q4.time_next_launch(a, b)
+            mfmas = q4.reference_mfma(mode, iterations, dev)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) / 1e3)
+        t = float(np.median(ts))
+        tf = mfmas * 16384 / t / 1e12
+        out[key] = {"TFLOPs": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                    "us": round(t * 1e6, 1)}
+    return out
+
+
 def time_floor(runner, steps, warmup, dev):
     """The decode step's launch structure without its arithmetic: a graph of
     one reference read per launch over that launch's weight bytes, and a graph
@@ -721,6 +772,14 @@ def main():
         }
         out["prefill"] = {"value": wl["4"]["TFLOPs_per_step"], "unit": "TFLOP/s", "roofline": wl["4"]["roofline"]}
         log(f"prefill: {tflops:.1f} TFLOP/s (kernel {pach:.1f})")
+        ceil = time_ceiling(dev)
+        out["prefill"]["arithmetic_ceiling"] = {
+            "workload": "the 128-row GEMM tiles' inner loop on register operands (q4_0_reference_mfma): "
+                        "8 MFMAs per B fragment, 4 waves per SIMD, no memory traffic",
+            **ceil,
+            "kernel_own_over_ceiling": round(pach / ceil["mfma_rescale_decode"]["TFLOPs"], 3),
+        }
+        log(f"arithmetic ceiling: {out['prefill']['arithmetic_ceiling']}")
         if do_cpu:
             spec = pspecs[0]
             rows = 1024

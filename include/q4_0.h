@@ -288,9 +288,30 @@ q4_status q4_0_reference_read(const void *src, int64_t bytes, void *sink, void *
 int64_t q4_0_reference_read_words(int64_t bytes);
 
 /*
+ * Measurement support: the prefill GEMM's arithmetic alone.  Each wave runs
+ * `iterations` rounds of the 128-row GEMM tiles' inner loop on operands held
+ * in registers -- 4 blocks, each 8 v_mfma_f32_16x16x32_bf16 sharing one B
+ * fragment -- with no loads, stores or barriers, at 4 waves per SIMD:
+ *   mode 0: the MFMAs alone, accumulating in the matrix pipe;
+ *   mode 1: each MFMA's result rescaled into the fp32 accumulators by the
+ *           block's scale (four FMAs per MFMA), as the exact method needs;
+ *   mode 2: mode 1 plus the decode of each block's B fragment from its codes.
+ * A launch runs q4_0_reference_mfma_threads() threads (4 workgroups of 256
+ * per compute unit) and issues threads / 64 * iterations * 32 MFMAs of
+ * 16 * 16 * 32 multiply-adds each; each thread writes one float to sink
+ * (device memory of that many floats, 4-byte aligned).  1 <= iterations <=
+ * 2^24, 0 <= mode <= 2.  Not a step of the method: a benchmark uses it to
+ * put the GEMM next to what its arithmetic allows apart from memory (the
+ * pages weigh compute against bandwidth for this layer: Rust fork, "Why L0
+ * Is Faster").  Asynchronous on stream; q4_0_time_next_launch applies to it.
+ */
+q4_status q4_0_reference_mfma(int mode, int64_t iterations, float *sink, void *stream);
+int64_t q4_0_reference_mfma_threads(void);
+
+/*
  * Measurement hook for benchmarks.  Arms the calling thread's next
  * q4_0_linear / q4_0_linear_multi / q4_0_linear_swiglu / q4_0_embed / q4_0_embed_gguf /
- * q4_1_linear / q4_0_reference_read launch so that
+ * q4_1_linear / q4_0_reference_read / q4_0_reference_mfma launch so that
  * its kernel records
  * `start_event` when it starts executing and `stop_event` when it finishes
  * (hipExtLaunchKernelGGL); hipEventElapsedTime on the pair is then that

@@ -30,6 +30,7 @@ from ._binding import (  # noqa: F401
     q41_pack,
     q41_packed_bytes,
     q41_quantize,
+    reference_mfma,
     reference_read,
     status_str,
     time_next_launch,

@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "Q4_OK", 1: "Q4_ERR_NULL", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIG
 EXPORTS = ("q4_status_str", "q4_0_packed_bytes", "q4_0_quantize", "q4_0_quantize_bf16", "q4_0_pack", "q4_0_unpack",
            "q4_0_dequant", "q4_0_linear", "q4_0_linear_multi", "q4_0_time_next_launch",
            "q4_0_linear_kernel", "q4_0_linear_swiglu", "q4_0_linear_swiglu_kernel", "q4_0_embed",
-           "q4_0_embed_gguf", "q4_0_reference_read", "q4_0_reference_read_words", "q4_1_packed_bytes",
+           "q4_0_embed_gguf", "q4_0_reference_read", "q4_0_reference_read_words", "q4_0_reference_mfma",
+           "q4_0_reference_mfma_threads", "q4_1_packed_bytes",
            "q4_1_quantize", "q4_1_pack", "q4_1_dequant", "q4_1_linear", "q4_1_linear_kernel")
 
 
@@ -84,6 +85,10 @@ def lib() -> ctypes.CDLL:
             L.q4_0_reference_read.restype = i32
             L.q4_0_reference_read_words.argtypes = [i64]
             L.q4_0_reference_read_words.restype = i64
+            L.q4_0_reference_mfma.argtypes = [i32, i64, vp, vp]
+            L.q4_0_reference_mfma.restype = i32
+            L.q4_0_reference_mfma_threads.argtypes = []
+            L.q4_0_reference_mfma_threads.restype = i64
             L.q4_1_packed_bytes.argtypes = [i64, i64]
             L.q4_1_packed_bytes.restype = ctypes.c_size_t
             for fn in (L.q4_1_quantize, L.q4_1_pack, L.q4_1_dequant):
@@ -341,6 +346,23 @@ def reference_read(src: torch.Tensor, nbytes: int | None = None, sink: torch.Ten
         _check(lib().q4_0_reference_read(src.data_ptr(), nbytes, sink.data_ptr(), _stream(src.device)),
                "q4_0_reference_read")
     return sink
+
+
+def reference_mfma(mode: int, iterations: int, device="cuda", sink: torch.Tensor | None = None) -> int:
+    """Measurement support: one launch of the prefill GEMM's arithmetic
+    alone (mode 0: MFMAs; 1: + the fp32 rescale; 2: + the decode) on the
+    current stream of `device`; returns the number of 16x16x32 MFMAs it
+    issues (each 16384 flops)."""
+    device = torch.device(device)
+    with torch.cuda.device(device):
+        threads = int(lib().q4_0_reference_mfma_threads())   # from the current device's CU count
+        if sink is None:
+            sink = torch.empty(threads, dtype=torch.float32, device=device)
+        if not sink.is_cuda or sink.dtype != torch.float32 or sink.numel() < threads:
+            raise ValueError(f"sink must be a device float32 tensor of at least {threads} elements")
+        _check(lib().q4_0_reference_mfma(int(mode), int(iterations), sink.data_ptr(), _stream(device)),
+               "q4_0_reference_mfma")
+    return threads // 64 * int(iterations) * 32
 
 
 # ------------------------------------------------ the asymmetric variant

@@ -265,6 +265,15 @@ q4_status q4_0_reference_read(const void *src, int64_t bytes, void *sink, void *
     return from_hip(q4::launch_reference_read(src, bytes, static_cast<uint32_t *>(sink), as_stream(stream)));
 }
 
+int64_t q4_0_reference_mfma_threads(void) { return q4::reference_mfma_threads(); }
+
+q4_status q4_0_reference_mfma(int mode, int64_t iterations, float *sink, void *stream) {
+    if (mode < 0 || mode > 2 || iterations < 1 || iterations > (int64_t(1) << 24)) return Q4_ERR_SHAPE;
+    if (!sink) return Q4_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(sink) & 3u) return Q4_ERR_ALIGN;
+    return from_hip(q4::launch_reference_mfma(mode, static_cast<int>(iterations), sink, as_stream(stream)));
+}
+
 q4_status q4_0_time_next_launch(void *start_event, void *stop_event) {
     q4::arm_launch_events(reinterpret_cast<hipEvent_t>(start_event), reinterpret_cast<hipEvent_t>(stop_event));
     return Q4_OK;

@@ -87,6 +87,11 @@ const char *linear_glu_config_name(int64_t M, int64_t K);
 int64_t reference_read_workgroups(int64_t bytes);
 hipError_t launch_reference_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
 
+// The prefill GEMM's arithmetic alone (measurement support): threads of a
+// launch (sink holds one float per thread) and the launch, mode 0-2.
+int64_t reference_mfma_threads();
+hipError_t launch_reference_mfma(int mode, int iters, float *sink, hipStream_t s);
+
 // Makes the calling thread's next linear, gated or embedding launch record
 // `start` / `stop` at its kernel's start and end.
 void arm_launch_events(hipEvent_t start, hipEvent_t stop);

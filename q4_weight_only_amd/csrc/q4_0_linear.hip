@@ -1763,4 +1763,80 @@ hipError_t launch_linear_q41(LinearArgs a, hipStream_t s) {
     }
 }
 
+// ------------------------------------------------------------- measurement
+// The prefill GEMM's arithmetic and nothing else: per wave the 128-row
+// tiles' 8 x 1 register tile (8 m-tiles sharing one B fragment per block),
+// operands in registers, no loads, stores or barriers, 4 waves per SIMD as in
+// the GEMM.  MODE 0: the MFMAs alone, accumulating in the matrix pipe;
+// MODE 1: each MFMA's result rescaled into acc by the block's scale in fp32
+// (four FMAs, issued after the next MFMA, as in gemm3_kernel); MODE 2: MODE 1
+// plus the decode of each block's B fragment from its codes.  The operands
+// pass through an empty asm statement each iteration, so no MFMA or decode
+// is loop-invariant.  What it shows: the rate the exact arithmetic allows on
+// this chip, apart from memory.
+namespace {
+constexpr int kCeilThreads = 256;
+constexpr int kCeilPerCU = 4;   // 256-thread workgroups per CU: 4 waves per SIMD
+
+template <int MODE>
+__global__ __launch_bounds__(kCeilThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void ceiling_kernel(float *sink, int iters) {
+    const uint32_t t = threadIdx.x + blockIdx.x * kCeilThreads;
+    bf16x8 A[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) A[mt][e] = static_cast<__bf16>(static_cast<float>(static_cast<int>((t + 3 * mt + e) & 7) - 3));
+    bf16x8 Bfix[kTileBlocks];   // modes 0 and 1: a distinct fragment per block
+#pragma unroll
+    for (int i = 0; i < kTileBlocks; ++i) Bfix[i] = A[(t + i) & 7];
+    u32x4 nib = (u32x4){t * 2654435761u, t * 40503u + 1u, t ^ 0x5bd1e995u, t * 7u + 3u};
+    u32x2 sc = (u32x2){0x3C003800u, 0x34003000u};   // fp16 1, 0.5, 0.25, 0.125
+    floatx4 acc[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) acc[mt] = (floatx4){0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+        asm volatile("" : "+v"(nib), "+v"(sc), "+v"(Bfix[0]), "+v"(Bfix[1]), "+v"(Bfix[2]), "+v"(Bfix[3]));
+#pragma unroll
+        for (int i = 0; i < kTileBlocks; ++i) {
+            const bf16x8 B = MODE == 2 ? decode_piece(piece_of(nib, i)) : Bfix[i];
+            if constexpr (MODE == 0) {
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt], B, acc[mt], 0, 0, 0);
+            } else {
+                const float d = scale_of(sc, i);
+                floatx4 D[8];
+                D[0] = mfma_block(A[0], B);
+#pragma unroll
+                for (int mt = 1; mt < 8; ++mt) {
+                    D[mt] = mfma_block(A[mt], B);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[mt - 1][r] = fmaf(d, D[mt - 1][r], acc[mt - 1][r]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[7][r] = fmaf(d, D[7][r], acc[7][r]);
+            }
+            if (i % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    float f = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) f += acc[mt][0] + acc[mt][1] + acc[mt][2] + acc[mt][3];
+    sink[t] = f;
+}
+}  // namespace
+
+int64_t reference_mfma_threads() { return static_cast<int64_t>(device_cus()) * kCeilPerCU * kCeilThreads; }
+
+hipError_t launch_reference_mfma(int mode, int iters, float *sink, hipStream_t s) {
+    const dim3 grid(static_cast<uint32_t>(device_cus() * kCeilPerCU)), block(kCeilThreads);
+    auto kernel = mode == 0 ? ceiling_kernel<0> : mode == 1 ? ceiling_kernel<1> : ceiling_kernel<2>;
+    hipEvent_t start = nullptr, stop = nullptr;
+    if (take_launch_events(start, stop))
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, start, stop, 0, sink, iters);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, s, sink, iters);
+    return hipGetLastError();
+}
+
 }  // namespace q4

@@ -238,6 +238,16 @@ def test_reference_read_validates_first(L):
     assert rr(FAKE, 64, FAKE + 2, None) == ALIGN
 
 
+def test_reference_mfma_validates_first(L):
+    rm = L.q4_0_reference_mfma
+    assert rm(3, 10, FAKE, None) == SHAPE                # modes 0-2 only
+    assert rm(-1, 10, FAKE, None) == SHAPE
+    assert rm(0, 0, FAKE, None) == SHAPE                 # at least one iteration
+    assert rm(2, 2**24 + 1, FAKE, None) == SHAPE
+    assert rm(1, 10, None, None) == NULL
+    assert rm(1, 10, FAKE + 2, None) == ALIGN
+
+
 @pytest.mark.parametrize("n,k", [(4096, 3072), (40, 384), (1, 32), (17, 96)])
 def test_q41_packed_bytes_matches_layout_definition(L, n, k):
     assert q4.q41_packed_bytes(n, k) == O.q41_packed_bytes(n, k)
