@@ -560,9 +560,12 @@ def time_floor(runner, steps, warmup, dev):
         def __init__(self, empty):
             self.empty = empty
 
+        def launch(self, i):
+            q4.reference_read(buf[offs[i]:offs[i] + sizes[i]], 0 if self.empty else sizes[i], sink)
+
         def step(self):
-            for off, n in zip(offs, sizes):
-                q4.reference_read(buf[off:off + n], 0 if self.empty else n, sink)
+            for i in range(len(sizes)):
+                self.launch(i)
 
     out = {}
     for key, empty in (("read_us_per_step", False), ("empty_us_per_step", True)):
@@ -571,6 +574,12 @@ def time_floor(runner, steps, warmup, dev):
         del g
         out[key] = round(el / steps * 1e6, 1)
         out[key.replace("_us_per_step", "_p10_p50_p90_us")] = pctl_us(r.step_times)
+    # each op's plain read on its own: kernel-own p10 / p50 / p90 over the layers and steps
+    per = time_kernels(Reads(False), steps, dev)
+    by_op = collections.defaultdict(list)
+    for (spec, *_), d in zip(runner.items, per):
+        by_op[spec.name.split(".", 1)[1]].extend(d)
+    out["per_op_read_us_p10_p50_p90"] = {op: pctl_us(d) for op, d in by_op.items()}
     out["launches"] = len(sizes)
     out["read_bytes_per_step"] = sum(sizes)
     out["read_GBs"] = round(sum(sizes) / (out["read_us_per_step"] * 1e-6) / 1e9, 1)

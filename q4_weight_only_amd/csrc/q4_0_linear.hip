@@ -1,38 +1,42 @@
 // The fused Q4_0 linear: y = x * W^T with W in the packed layout of
-// include/q4_0.h, x bf16, y fp32.
+// include/q4_0.h, x bf16, y fp32; the gated (SwiGLU) launch; the asymmetric
+// variant (w = q d + m); and the arithmetic-only measurement loop.
 //
-// Arithmetic (identical in both kernels).  A 16x16x32 bf16 MFMA covers one
-// Q4_0 block (32 k) for 16 output rows x 16 weight rows.  Its B operand is
-// the block's codes decoded exactly to bf16 (q - 8) / 16 -- v_cvt_off_f32_i4
-// turns a 4-bit two's-complement code c into c / 16, which is why the packed
-// layout stores q XOR 8 -- and its A operand is x itself, so every product is
-// exact and the MFMA sums the block in fp32.  The block result is then scaled
-// by the block's fp16 d in fp32 (one FMA per output element per block) and
-// the final sum is multiplied by 16.  This is the pages' fused
-// dequant + matmul (hakusoku summary, "線形演算・埋め込み") with the
-// dequantization split so that no weight is ever rounded.
+// Arithmetic (identical in every linear kernel).  A 16x16x32 bf16 MFMA covers
+// one Q4_0 block (32 k) for 16 output rows x 16 weight rows.  Its B operand
+// is the block's codes decoded exactly to bf16 (q - 8) / 16 --
+// v_cvt_off_f32_i4 turns a 4-bit two's-complement code c into c / 16, which
+// is why the packed layout stores q XOR 8 -- and its A operand is x itself,
+// so every product is exact and the MFMA sums the block in fp32.  The block
+// result is then scaled by the block's fp16 d in fp32 (one FMA per output
+// element per block) and the final sum is multiplied by 16.  This is the
+// pages' fused dequant + matmul (hakusoku summary, "線形演算・埋め込み") with
+// the dequantization split so that no weight is ever rounded.
 //
 // Kernels.
-//   skinny_kernel  (M <= 16, decode-sized batches; also 17-64 rows when the
-//                  weights are short): a wave owns all M rows,
-//                  NT 16-row weight tiles and every WK-th super-tile along K;
-//                  weights go straight from HBM into MFMA B registers (each
-//                  lane's 16-byte load is exactly its B slice for 4 blocks),
-//                  x comes from LDS (staged once) or global memory, and the WK
-//                  waves of a workgroup are summed through LDS in a fixed order.
-//   skinny_stream_kernel (M = 1, very tall weights): the same per tile, with a
-//                  fixed grid walking the tiles.
-//   gemm_kernel    (17 <= M <= 64, tall weights): a workgroup tile of BM x BN outputs; the x
-//                  tile of each 128-k step is staged in LDS (double-buffered,
-//                  XOR-swizzled 16-byte chunks) and shared by the WN waves;
-//                  weights again go HBM -> registers.
+//   gemv_kernel    (M <= 4, K <= 4096: the decode step's QKV, O and gate/up):
+//                  a workgroup owns one 16-row weight tile and all M rows, its
+//                  WK waves split K; each wave issues x and then every one of
+//                  its weight stages at once and consumes them as they land.
+//   skinny_kernel  (other M <= 16, and 17-64 rows when the weights are
+//                  short): the same work split with a P-deep refill of each
+//                  wave's stages; x from LDS (staged once) or global memory.
+//   skinny_stream_kernel (M = 1, very tall weights): the same per tile, with
+//                  a fixed grid walking the tiles.
+//   gemm_kernel    (17 <= M <= 64, tall weights): a workgroup tile of BM x BN
+//                  outputs; the x tile of each 128-k step is staged in LDS
+//                  (double-buffered, XOR-swizzled 16-byte chunks) and shared
+//                  by the WN waves; weights go HBM -> registers.
 //   gemm3_kernel   (M > 64, prefill / encoder sizes): the same arithmetic with
 //                  MT x NT register tiles per wave, x staged a quarter per
 //                  block step through bounds-checked buffer loads, and an
 //                  XCD-aware workgroup -> tile order.
+// In every kernel the weights go straight from HBM into MFMA B registers
+// (each lane's 16-byte load is exactly its B slice for 4 blocks) and the
+// partial sums of a K split are added through LDS in a fixed order.
 // gemm_kernel and gemm3_kernel add the block results of an output in the same
-// order, so they give bitwise equal results for any tiling.
-// No kernel uses atomics: results are bitwise reproducible.
+// order, so they give bitwise equal results for any tiling.  No kernel uses
+// atomics: results are bitwise reproducible.
 
 #include <atomic>
 #include <string>
