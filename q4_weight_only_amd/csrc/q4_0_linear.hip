@@ -1477,24 +1477,27 @@ bool take_launch_events(hipEvent_t &start, hipEvent_t &stop) {
 // that many waves stay resident (the launches are latency-bound); long rows
 // (K > 3072) split K wider; one row over very tall weights walks the tiles
 // with a fixed grid.  17-64 rows choose between the K-split kernel and the
-// GEMM by tile count (pick_17_64).  Above 64 rows three GEMM tile shapes compete on
-// how evenly their work tiles spread over the device's compute units:
+// GEMM by tile count (pick_17_64).  Above 64 rows four GEMM tile shapes compete
+// on how evenly their work tiles spread over the device's compute units:
 //   gemm3 64 x 128   (two workgroups per CU),
 //   gemm3 128 x 128  (two workgroups per CU),
-//   gemm3 128 x 192  (12 waves, one workgroup per CU).
+//   gemm3 128 x 192  (12 waves, one workgroup per CU),
+//   gemm3 96 x 192   (12 waves, one workgroup per CU).
 // A launch costs about ceil(tiles / CUs) x the time of one tile on a fully
 // occupied CU; measured on MI355X at M = 1505, 2048 and 6020 over the decoder,
-// adapter and encoder shapes, those per-tile times are 0.30 : 0.50 : 0.85
-// (the 128-row tiles' unit), and the smallest estimate wins (a tie goes to
-// 128 x 128, then to 64 x 128).  This puts N = 3072 at
-// M = 2048 (384 tiles of 128 x 128 on 256 CUs, a last round half empty) on
-// exactly 256 tiles of 128 x 192.  Every GEMM tile shape adds the block
+// adapter and encoder shapes, those per-tile times are 0.30 : 0.50 : 0.85 :
+// 0.79 (the 128-row tiles' unit; 96 x 192 from the M = 1505 adapter shapes,
+// where its 256 tiles ran 6-7% faster than 192 tiles of 128 x 192), and the
+// smallest estimate wins (a tie goes to 128 x 128, then to 64 x 128, then to
+// 128 x 192).  This puts N = 3072 at M = 2048 (384 tiles of 128 x 128 on 256
+// CUs, a last round half empty) on exactly 256 tiles of 128 x 192, and at
+// M = 1505 on 256 tiles of 96 x 192.  Every GEMM tile shape adds the block
 // results of an output in the same order, so the choice never changes a
 // result.
 namespace {
 enum class Cfg { G1, G1K, G2, G2K, G4, G4K, M1Stream, M1Long, M2Long, M4Long, M16, M16Long, M32, M32Split, M32Split2,
                  M64, M64Split,
-                 Gemm64, Gemm128, Gemm128W };
+                 Gemm64, Gemm128, Gemm128W, Gemm96W };
 
 // Configuration by M and K alone: the decode sizes, and the gated launch's
 // GEMM split at 2048 rows.
@@ -1557,9 +1560,11 @@ Cfg pick_17_64(const LinearArgs &a, Cfg gemm) {
 Cfg gemm_shape(const LinearArgs &a) {
     const int64_t cus = device_cus();
     auto cost = [&](int bm, int bn, int64_t unit) { return (gemm_tiles(a, bm, bn) + cus - 1) / cus * unit; };
-    const int64_t c64 = cost(64, 128, 30), c128 = cost(128, 128, 50), c128w = cost(128, 192, 85);
-    if (c128 <= c64 && c128 <= c128w) return Cfg::Gemm128;
-    return c64 <= c128w ? Cfg::Gemm64 : Cfg::Gemm128W;
+    const int64_t c64 = cost(64, 128, 30), c128 = cost(128, 128, 50), c128w = cost(128, 192, 85),
+                  c96w = cost(96, 192, 79);
+    if (c128 <= c64 && c128 <= c128w && c128 <= c96w) return Cfg::Gemm128;
+    if (c64 <= c128w && c64 <= c96w) return Cfg::Gemm64;
+    return c128w <= c96w ? Cfg::Gemm128W : Cfg::Gemm96W;
 }
 
 Cfg pick(const LinearArgs &a) {
@@ -1638,6 +1643,7 @@ const char *linear_config_name(const LinearArgs &a) {
         case Cfg::M64Split: return skinny_name(M, K, 64, "skinny_kernel<64, 1, 8, 2, true, 0, false>", "skinny_kernel<64, 1, 8, 2, false, 0, false>");
         case Cfg::Gemm64: return "gemm3_kernel<4, 1, 1, 8, 4, 8, false>";
         case Cfg::Gemm128W: return "gemm3_kernel<8, 1, 1, 12, 0, 4, false>";
+        case Cfg::Gemm96W: return "gemm3_kernel<6, 1, 1, 12, 0, 4, false>";
         default: return "gemm3_kernel<8, 1, 1, 8, 4, 4, false>";
     }
 }
@@ -1663,6 +1669,7 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
         case Cfg::M64Split: return run_skinny<64, 1, 8, 2, 0>(a, s);
         case Cfg::Gemm64: return run_gemm3<4, 1, 1, 8, 4, 8>(a, s);
         case Cfg::Gemm128W: return run_gemm3<8, 1, 1, 12, 0, 4>(a, s);
+        case Cfg::Gemm96W: return run_gemm3<6, 1, 1, 12, 0, 4>(a, s);
         default: return run_gemm3<8, 1, 1, 8, 4, 4>(a, s);
     }
 }
@@ -1730,7 +1737,8 @@ Q41 pick_q41(const LinearArgs &a) {
     if (a.M <= 64) return Q41::Gemm64r;
     switch (gemm_shape(a)) {
         case Cfg::Gemm64: return Q41::Gemm64;
-        case Cfg::Gemm128W: return Q41::Gemm128W;
+        case Cfg::Gemm128W:
+        case Cfg::Gemm96W: return Q41::Gemm128W;
         default: return Q41::Gemm128;
     }
 }

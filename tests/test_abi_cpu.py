@@ -165,6 +165,7 @@ def test_linear_kernel_names(L):
     assert kn(1, 3072, arr(131072), 1) == b"skinny_stream_kernel<1, 8, 3, 6>"
     assert kn(1, 3072, arr(9216, 9216), 2) == b"gemv_kernel<1, 8, 3, 6, false>"
     assert kn(2048, 4096, arr(3072), 1) == b"gemm3_kernel<8, 1, 1, 12, 0, 4, false>"
+    assert kn(1505, 5120, arr(3072), 1) == b"gemm3_kernel<6, 1, 1, 12, 0, 4, false>"   # 256 tiles of 96 x 192
     assert kn(2048, 3072, arr(3072, 3072, 3072), 3) == b"gemm3_kernel<8, 1, 1, 8, 4, 4, false>"
     assert kn(300, 3072, arr(3072), 1) == b"gemm3_kernel<4, 1, 1, 8, 4, 8, false>"
 

@@ -67,13 +67,14 @@ def test_tile_shapes_agree_bitwise():
 
 def test_tile_shape_names():
     """At 2048 rows on 256 CUs: N = 3072 alone fills exactly 256 tiles of
-    128 x 192; three of them fused make 1152 tiles of 128 x 128; few rows
-    take 64 x 128."""
+    128 x 192; three of them fused make 1152 tiles of 128 x 128; at 1505 rows
+    N = 3072 fills 256 tiles of 96 x 192; few rows take 64 x 128."""
     import torch
     cus = torch.cuda.get_device_properties(DEV).multi_processor_count
     if cus != 256:
         pytest.skip(f"tile counts here assume 256 compute units, the device has {cus}")
     assert q4.linear_kernel(2048, 4096, 3072) == "gemm3_kernel<8, 1, 1, 12, 0, 4, false>"
+    assert q4.linear_kernel(1505, 3072, 3072) == "gemm3_kernel<6, 1, 1, 12, 0, 4, false>"
     assert q4.linear_kernel(2048, 3072, (3072, 3072, 3072)) == "gemm3_kernel<8, 1, 1, 8, 4, 4, false>"
     assert q4.linear_kernel(2048, 3072, (9216, 9216)) == "gemm3_kernel<8, 1, 1, 8, 4, 4, false>"
     assert q4.linear_kernel(300, 3072, 3072) == "gemm3_kernel<4, 1, 1, 8, 4, 8, false>"
