@@ -117,3 +117,27 @@ def test_gemm_tile_shapes_agree_bitwise():
             part = q4.q41_linear(x[:m], pw)
             assert torch.equal(part.view(torch.int32), full[:m].view(torch.int32)), f"K={k} M={m}"
         assert len(names) >= 3, names
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(4100 + seed)
+    m = int(rng.choice([1, 2, 3, 4, 5, 17, 33, 64, 65, 129, 300, 1500]))
+    k = 32 * int(rng.integers(1, 161))
+    n = int(rng.integers(1, 1600))
+    while m * n * k > 4e7:
+        n = max(1, n // 2)
+    return m, k, n
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_launch_within_bound(seed):
+    """Seeded random shapes across the asymmetric dispatch (every kernel
+    family, ragged N, any K that is a multiple of 32 up to 5120): every
+    output element against the oracle's bound."""
+    m, k, n = _random_case(seed)
+    pw, ref = _weights(n, k, 7, seed)
+    xb = inputs.activations_bf16((m, k), seed=7, tags=(41, seed, m, k))
+    say("q41 random", seed, m, k, n, q4.q41_linear_kernel(m, k, n))
+    y = q4.q41_linear(to_dev_x(xb), pw).cpu().numpy()
+    yr, bound = O.q41_linear_with_bound(xb, ref, n, k)
+    assert_within_bound(y, yr, bound, f"q41 random {seed}: M={m} N={n} K={k}")
