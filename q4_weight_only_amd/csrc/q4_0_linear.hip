@@ -954,14 +954,13 @@ struct Gemm3Cfg {
 // each block's product D is rescaled by d as in the symmetric kernel; the
 // offsets' share, sum over blocks b of m[n, b] S[row, b] with S the block
 // sums of x, is itself a small product, taken on the matrix cores once per
-// 8 blocks.  Per 128-k step, wave w < MT computes S for m-tile w (four
-// MFMAs against its x fragments, block i with A rows 4i .. 4i + 3 set to
-// ones, leave S[row r, block g] in lane 16 g + r) and stores S split into
-// bf16 hi + lo in LDS; per 8 blocks every wave
-// builds MFMA A fragments from them and multiplies by its rows' offsets,
-// split the same way (exactly: fp16 has 11 significant bits), accumulating
-// into acc: k = 4 b + t pairs (S_hi, m_hi), (S_hi, m_lo), (S_lo, m_hi),
-// (S_lo, m_lo).
+// 8 blocks.  Per 128-k step, wave w computes S for m-tile w % MT (four MFMAs
+// against its x fragments -- block i with A rows 4i .. 4i + 3 set to ones --
+// leave S[row r, block g] in lane 16 g + r) and stores S split into bf16
+// hi + lo in LDS; per 8 blocks every wave builds MFMA A fragments from them
+// and multiplies by its rows' offsets, split the same way (exactly: fp16 has
+// 11 significant bits), accumulating into acc with k = 4 b + t running over
+// the pairs (S_hi, m_hi), (S_hi, m_lo), (S_lo, m_hi), (S_lo, m_lo).
 template <int MT, int NT, int WM, int WN, int WPE, int GM, bool GLU, bool ASYM = false>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
 void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
