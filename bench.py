@@ -240,7 +240,8 @@ def time_swiglu(prepared, ms, reps, dev):
     every launch reads its weights from HBM, not from the infinity cache.
     Two more kinds are timed by events recorded on the stream around the
     calls (launch gaps included): the fused launch, and the unfused launch
-    followed by torch's silu(g) * u into h (the unfused step in full)."""
+    followed by torch's silu(g) * u into h (the unfused step in full).
+    Each kind's time is the median over its launches."""
     import numpy as np
     import torch
 
@@ -285,7 +286,7 @@ def time_swiglu(prepared, ms, reps, dev):
                     if r > 0:              # the first pass warms up
                         pairs[kind].append((a, b))
         torch.cuda.synchronize(dev)
-        t = {kind: float(np.mean([a.elapsed_time(b) / 1e3 for a, b in v])) for kind, v in pairs.items()}
+        t = {kind: float(np.median([a.elapsed_time(b) / 1e3 for a, b in v])) for kind, v in pairs.items()}
         wbytes = spec0.weight_bytes()
         fused_bytes = wbytes + m * k * 2 + m * n * 4
         unfused_bytes = wbytes + m * k * 2 + 2 * m * n * 4
