@@ -300,7 +300,8 @@ int64_t q4_0_reference_read_words(int64_t bytes);
  * per compute unit) and issues threads / 64 * iterations * 32 MFMAs of
  * 16 * 16 * 32 multiply-adds each; each thread writes one float to sink
  * (device memory of that many floats, 4-byte aligned).  1 <= iterations <=
- * 2^24, 0 <= mode <= 2.  Not a step of the method: a benchmark uses it to
+ * 2^20 (one iteration takes about a microsecond on MI355X), 0 <= mode <= 2.
+ * Not a step of the method: a benchmark uses it to
  * put the GEMM next to what its arithmetic allows apart from memory (the
  * pages weigh compute against bandwidth for this layer: Rust fork, "Why L0
  * Is Faster").  Asynchronous on stream; q4_0_time_next_launch applies to it.

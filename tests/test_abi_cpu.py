@@ -244,7 +244,7 @@ def test_reference_mfma_validates_first(L):
     assert rm(3, 10, FAKE, None) == SHAPE                # modes 0-2 only
     assert rm(-1, 10, FAKE, None) == SHAPE
     assert rm(0, 0, FAKE, None) == SHAPE                 # at least one iteration
-    assert rm(2, 2**24 + 1, FAKE, None) == SHAPE
+    assert rm(2, 2**20 + 1, FAKE, None) == SHAPE
     assert rm(1, 10, None, None) == NULL
     assert rm(1, 10, FAKE + 2, None) == ALIGN
 
