@@ -241,7 +241,10 @@ def time_swiglu(prepared, ms, reps, dev):
     Two more kinds are timed by events recorded on the stream around the
     calls (launch gaps included): the fused launch, and the unfused launch
     followed by torch's silu(g) * u into h (the unfused step in full).
-    Each kind's time is the median over its launches."""
+    Each kind's time is the median over its launches; two untimed passes
+    over every kind come first (the GPU has been idle through the host-side
+    oracle timing before this, and a single pass left the first kind's
+    launches up to a third slower in some runs)."""
     import numpy as np
     import torch
 
@@ -260,7 +263,7 @@ def time_swiglu(prepared, ms, reps, dev):
         ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for _ in range(2)]
         kinds = ("fused", "fused_bf16", "unfused", "fused_stream", "unfused_silu_stream")
         pairs = {kind: [] for kind in kinds}
-        for r in range(reps + 1):
+        for r in range(reps + 2):
             for kind in kinds:
                 for _, pws in gate_up:
                     a = torch.cuda.Event(enable_timing=True)
@@ -283,7 +286,7 @@ def time_swiglu(prepared, ms, reps, dev):
                             q4.linear_swiglu(x, pws[0], pws[1], h16, dtype=torch.bfloat16)
                         else:
                             q4.linear_multi(x, pws, ys)
-                    if r > 0:              # the first pass warms up
+                    if r > 1:              # the first two passes warm up
                         pairs[kind].append((a, b))
         torch.cuda.synchronize(dev)
         t = {kind: float(np.median([a.elapsed_time(b) / 1e3 for a, b in v])) for kind, v in pairs.items()}
