@@ -517,8 +517,10 @@ def cpu_oracle_rate(jobs, runs, unit, sample):
 # ---------------------------------------------------------- decode floor
 def time_ceiling(dev, iterations=2000, reps=5):
     """The prefill GEMM's arithmetic alone (q4_0_reference_mfma): kernel-own
-    TFLOP/s of the MFMAs, of the MFMAs with the exact fp32 rescale, and of
-    both with the nibble decode, median of `reps` launches each."""
+    TFLOP/s of the MFMAs, of the MFMAs with the exact fp32 rescale, of both
+    with the nibble decode, and of the MFMAs beside as many fp32 FMAs that do
+    not depend on them (can the rescale's VALU work hide under the MFMAs?),
+    median of `reps` launches each."""
     import numpy as np
     import torch
 
@@ -526,7 +528,8 @@ def time_ceiling(dev, iterations=2000, reps=5):
 
     stream = torch.cuda.current_stream(dev)
     out = {}
-    for mode, key in ((0, "mfma_only"), (1, "mfma_rescale"), (2, "mfma_rescale_decode")):
+    for mode, key in ((0, "mfma_only"), (1, "mfma_rescale"), (2, "mfma_rescale_decode"),
+                      (3, "mfma_independent_fma")):
         q4.reference_mfma(mode, 10, dev)
         ts = []
         for _ in range(reps):

@@ -295,12 +295,14 @@ int64_t q4_0_reference_read_words(int64_t bytes);
  *   mode 0: the MFMAs alone, accumulating in the matrix pipe;
  *   mode 1: each MFMA's result rescaled into the fp32 accumulators by the
  *           block's scale (four FMAs per MFMA), as the exact method needs;
- *   mode 2: mode 1 plus the decode of each block's B fragment from its codes.
+ *   mode 2: mode 1 plus the decode of each block's B fragment from its codes;
+ *   mode 3: mode 0 plus four fp32 FMAs per MFMA on registers the MFMAs do not
+ *           touch (mode 1's VALU work without its dependence on the MFMAs).
  * A launch runs q4_0_reference_mfma_threads() threads (4 workgroups of 256
  * per compute unit) and issues threads / 64 * iterations * 32 MFMAs of
  * 16 * 16 * 32 multiply-adds each; each thread writes one float to sink
  * (device memory of that many floats, 4-byte aligned).  1 <= iterations <=
- * 2^20 (one iteration takes about a microsecond on MI355X), 0 <= mode <= 2.
+ * 2^20 (one iteration takes about a microsecond on MI355X), 0 <= mode <= 3.
  * Not a step of the method: a benchmark uses it to
  * put the GEMM next to what its arithmetic allows apart from memory (the
  * pages weigh compute against bandwidth for this layer: Rust fork, "Why L0

@@ -350,7 +350,8 @@ def reference_read(src: torch.Tensor, nbytes: int | None = None, sink: torch.Ten
 
 def reference_mfma(mode: int, iterations: int, device="cuda", sink: torch.Tensor | None = None) -> int:
     """Measurement support: one launch of the prefill GEMM's arithmetic
-    alone (mode 0: MFMAs; 1: + the fp32 rescale; 2: + the decode) on the
+    alone (mode 0: MFMAs; 1: + the fp32 rescale; 2: + the decode; 3: MFMAs
+    beside as many independent fp32 FMAs as the rescale) on the
     current stream of `device`; returns the number of 16x16x32 MFMAs it
     issues (each 16384 flops)."""
     device = torch.device(device)

@@ -268,7 +268,7 @@ q4_status q4_0_reference_read(const void *src, int64_t bytes, void *sink, void *
 int64_t q4_0_reference_mfma_threads(void) { return q4::reference_mfma_threads(); }
 
 q4_status q4_0_reference_mfma(int mode, int64_t iterations, float *sink, void *stream) {
-    if (mode < 0 || mode > 2 || iterations < 1 || iterations > (int64_t(1) << 20)) return Q4_ERR_SHAPE;
+    if (mode < 0 || mode > 3 || iterations < 1 || iterations > (int64_t(1) << 20)) return Q4_ERR_SHAPE;
     if (!sink) return Q4_ERR_NULL;
     if (reinterpret_cast<uintptr_t>(sink) & 3u) return Q4_ERR_ALIGN;
     return from_hip(q4::launch_reference_mfma(mode, static_cast<int>(iterations), sink, as_stream(stream)));

@@ -1781,10 +1781,13 @@ hipError_t launch_linear_q41(LinearArgs a, hipStream_t s) {
 // the GEMM.  MODE 0: the MFMAs alone, accumulating in the matrix pipe;
 // MODE 1: each MFMA's result rescaled into acc by the block's scale in fp32
 // (four FMAs, issued after the next MFMA, as in gemm3_kernel); MODE 2: MODE 1
-// plus the decode of each block's B fragment from its codes.  The operands
-// pass through an empty asm statement each iteration, so no MFMA or decode
-// is loop-invariant.  What it shows: the rate the exact arithmetic allows on
-// this chip, apart from memory.
+// plus the decode of each block's B fragment from its codes; MODE 3: MODE 0
+// with four fp32 FMAs per MFMA beside it on registers no MFMA reads or
+// writes (the same VALU work as MODE 1's rescale, with no dependence on the
+// matrix pipe).  The operands pass through an empty asm statement each
+// iteration, so no MFMA, FMA or decode is loop-invariant.  What it shows: the
+// rate the exact arithmetic allows on this chip, apart from memory, and
+// whether its VALU work could hide under the MFMAs.
 namespace {
 constexpr int kCeilThreads = 256;
 constexpr int kCeilPerCU = 4;   // 256-thread workgroups per CU: 4 waves per SIMD
@@ -1806,6 +1809,7 @@ void ceiling_kernel(float *sink, int iters) {
     floatx4 acc[8];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) acc[mt] = (floatx4){0.f, 0.f, 0.f, 0.f};
+    float side[4] = {1.f, 2.f, 3.f, 4.f};   // mode 3's FMA chains
     for (int it = 0; it < iters; ++it) {
         asm volatile("" : "+v"(nib), "+v"(sc), "+v"(Bfix[0]), "+v"(Bfix[1]), "+v"(Bfix[2]), "+v"(Bfix[3]));
 #pragma unroll
@@ -1814,6 +1818,14 @@ void ceiling_kernel(float *sink, int iters) {
             if constexpr (MODE == 0) {
 #pragma unroll
                 for (int mt = 0; mt < 8; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt], B, acc[mt], 0, 0, 0);
+            } else if constexpr (MODE == 3) {
+                const float d = scale_of(sc, i);
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt) {
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt], B, acc[mt], 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) side[r] = fmaf(d, side[r], static_cast<float>(r));
+                }
             } else {
                 const float d = scale_of(sc, i);
                 floatx4 D[8];
@@ -1830,7 +1842,7 @@ void ceiling_kernel(float *sink, int iters) {
             if (i % 2 == 1) __builtin_amdgcn_sched_barrier(0);
         }
     }
-    float f = 0.f;
+    float f = side[0] + side[1] + side[2] + side[3];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) f += acc[mt][0] + acc[mt][1] + acc[mt][2] + acc[mt][3];
     sink[t] = f;
@@ -1841,7 +1853,10 @@ int64_t reference_mfma_threads() { return static_cast<int64_t>(device_cus()) * k
 
 hipError_t launch_reference_mfma(int mode, int iters, float *sink, hipStream_t s) {
     const dim3 grid(static_cast<uint32_t>(device_cus() * kCeilPerCU)), block(kCeilThreads);
-    auto kernel = mode == 0 ? ceiling_kernel<0> : mode == 1 ? ceiling_kernel<1> : ceiling_kernel<2>;
+    auto kernel = mode == 0   ? ceiling_kernel<0>
+                  : mode == 1 ? ceiling_kernel<1>
+                  : mode == 2 ? ceiling_kernel<2>
+                              : ceiling_kernel<3>;
     hipEvent_t start = nullptr, stop = nullptr;
     if (take_launch_events(start, stop))
         hipExtLaunchKernelGGL(kernel, grid, block, 0, s, start, stop, 0, sink, iters);

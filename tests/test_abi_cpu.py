@@ -241,7 +241,7 @@ def test_reference_read_validates_first(L):
 
 def test_reference_mfma_validates_first(L):
     rm = L.q4_0_reference_mfma
-    assert rm(3, 10, FAKE, None) == SHAPE                # modes 0-2 only
+    assert rm(4, 10, FAKE, None) == SHAPE                # modes 0-3 only
     assert rm(-1, 10, FAKE, None) == SHAPE
     assert rm(0, 0, FAKE, None) == SHAPE                 # at least one iteration
     assert rm(2, 2**20 + 1, FAKE, None) == SHAPE

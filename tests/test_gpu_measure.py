@@ -33,7 +33,7 @@ def test_reference_read_of_nothing_is_one_launch():
     assert sink.numel() == 1 and int(sink[0]) == 0
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
 def test_reference_mfma_runs_deterministically(mode):
     say("reference mfma", mode)
     a = torch.empty(int(q4.lib().q4_0_reference_mfma_threads()), dtype=torch.float32, device=DEV)
