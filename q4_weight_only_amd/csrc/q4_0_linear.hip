@@ -299,7 +299,8 @@ void skinny_kernel(const LinearArgs a) {
         const int chunks_per_row = KT * (kTileK / 8);          // 16-byte chunks
         const int total = mrows * chunks_per_row;
         for (int c = threadIdx.x; c < total; c += C::kThreads) {
-            const int m = c / chunks_per_row, kc = c - m * chunks_per_row;
+            // a one-row launch has no row index to divide out
+            const int m = MROWS == 1 ? 0 : c / chunks_per_row, kc = c - m * chunks_per_row;
             u32x4 v = (u32x4){0u, 0u, 0u, 0u};
             if (kc * 8 < a.K) v = *reinterpret_cast<const u32x4 *>(a.x + static_cast<int64_t>(m) * a.K + kc * 8);
             *reinterpret_cast<u32x4 *>(xs + m * row_bytes + kc * 16) = v;
@@ -480,7 +481,9 @@ void gemv_kernel(const LinearArgs a) {
 #pragma unroll
     for (int q = 0; q < kXPer; ++q) {
         const int c = threadIdx.x + q * kThreads;
-        const int m = c / chunks_per_row, kc = c - m * chunks_per_row;
+        // the row index without an integer division at one and two rows
+        const int m = MROWS == 1 ? 0 : MROWS == 2 ? (c >= chunks_per_row ? 1 : 0) : c / chunks_per_row;
+        const int kc = c - m * chunks_per_row;
         const bool in = c < xtotal && kc * 8 < a.K;
         // a thread without a chunk stores its zeros to the pad slot after the tile
         xdst[q] = c < xtotal ? m * row_bytes + kc * 16 : mrows * row_bytes;
@@ -525,17 +528,21 @@ void gemv_kernel(const LinearArgs a) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         const bool live = wk + j * WK < KT;
+        // a stage past K adds zeros: its scales (and offsets) are zeroed once per stage
+        const u32x2 scj = live ? sc[j] : (u32x2){0u, 0u};
+        u32x2 moj = (u32x2){0u, 0u};
+        if constexpr (ASYM) moj = live ? mo[j] : (u32x2){0u, 0u};
 #pragma unroll
         for (int i = 0; i < kTileBlocks; ++i) {
             const int b = ktj[j] * kTileBlocks + i;
             const bf16x8 A = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xs + a_off + b * kQK * 2));
             const bf16x8 B = ASYM ? decode_piece_u(piece_of(nib[j], i)) : decode_piece(piece_of(nib[j], i));
-            const float d = live ? scale_of(sc[j], i) : 0.0f;
+            const float d = scale_of(scj, i);
             const floatx4 D = mfma_block(A, B);
 #pragma unroll
             for (int r = 0; r < REGS; ++r) acc[r] = fmaf(d, D[r], acc[r]);
             if constexpr (ASYM) {
-                const float m = live ? scale_of(mo[j], i) : 0.0f;
+                const float m = scale_of(moj, i);
                 const floatx4 S = mfma_block(A, bf16_ones());
 #pragma unroll
                 for (int r = 0; r < REGS; ++r) acc[r] = fmaf(m, S[r], acc[r]);
