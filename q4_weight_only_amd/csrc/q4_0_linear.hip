@@ -1618,7 +1618,7 @@ GemvCfg gemv_cfg(Cfg c) {
     switch (c) {
         case Cfg::G1: return {1, 8, 6};
         case Cfg::G1K: return {1, 16, 0};
-        case Cfg::G2: return {2, 4, 0};
+        case Cfg::G2: return {2, 8, 0};
         case Cfg::G2K: return {2, 8, 0};
         case Cfg::G4: return {4, 8, 0};
         default: return {4, 16, 0};   // G4K
@@ -1658,7 +1658,7 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
     switch (pick(a)) {
         case Cfg::G1: return run_gemv<1, 8, 6, false, 3>(a, s);
         case Cfg::G1K: return run_gemv<1, 16, 0, false, 2>(a, s);
-        case Cfg::G2: return run_gemv<2, 4, 0, false, 6>(a, s);
+        case Cfg::G2: return run_gemv<2, 8, 0, false, 3>(a, s);
         case Cfg::G2K: return run_gemv<2, 8, 0, false, 4>(a, s);
         case Cfg::G4: return run_gemv<4, 8, 0, false, 3>(a, s);
         case Cfg::G4K: return run_gemv<4, 16, 0, false, 2>(a, s);
@@ -1711,7 +1711,7 @@ hipError_t launch_linear_glu(LinearArgs a, hipStream_t s) {
     switch (pick_mk(a.M, a.K)) {
         case Cfg::G1: return run_gemv<1, 8, 6, true, 3>(a, s);
         case Cfg::G1K: return run_gemv<1, 16, 0, true, 2>(a, s);
-        case Cfg::G2: return run_gemv<2, 4, 0, true, 6>(a, s);
+        case Cfg::G2: return run_gemv<2, 8, 0, true, 3>(a, s);
         case Cfg::G2K: return run_gemv<2, 8, 0, true, 4>(a, s);
         case Cfg::G4: return run_gemv<4, 8, 0, true, 3>(a, s);
         case Cfg::G4K: return run_gemv<4, 16, 0, true, 2>(a, s);

@@ -144,7 +144,7 @@ def test_linear_kernel_names(L):
     assert kn(1, 3072, arr(4096, 1024, 1024), 3) == b"gemv_kernel<1, 8, 3, 6, false>"
     assert kn(1, 4096, arr(3072), 1) == b"gemv_kernel<1, 16, 2, 0, false>"
     assert kn(1, 9216, arr(3072), 1) == b"skinny_kernel<1, 1, 16, 2, true, 0, false>"   # long K
-    assert kn(2, 3072, arr(9216, 9216), 2) == b"gemv_kernel<2, 4, 6, 0, false>"
+    assert kn(2, 3072, arr(9216, 9216), 2) == b"gemv_kernel<2, 8, 3, 0, false>"
     assert kn(3, 1280, arr(512), 1) == b"gemv_kernel<4, 8, 2, 0, false>"
     assert L.q4_0_linear_swiglu_kernel(1, 3072) == b"gemv_kernel<1, 8, 3, 6, true>"
     assert L.q4_0_linear_swiglu_kernel(2, 4096) == b"gemv_kernel<2, 8, 4, 0, true>"
