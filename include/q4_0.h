@@ -271,8 +271,11 @@ const char *q4_1_linear_kernel(int64_t M, int64_t K, int64_t N);
  * Measurement support: a reference streaming read.  Reads `bytes` bytes at
  * src (device, 16-byte aligned, bytes a multiple of 16, 0 <= bytes <= 2^40)
  * with the 16-byte nontemporal loads the linear kernels use for weights, and
- * does nothing else with them (each workgroup of 256 threads reads 64 KiB and
- * writes one 32-bit word to sink, so the reads cannot be elided).  With
+ * does nothing else with them: workgroup b (256 threads) reads the 64 KiB
+ * from byte 65536 b, thread t the 16-byte chunks 4096 b + 256 p + t
+ * (p = 0 .. 15), and writes the XOR of their 32-bit words (zero past
+ * `bytes`) to sink word 256 b + t, so the reads cannot be elided; no
+ * cross-lane work, barrier or other step follows the loads.  With
  * bytes == 0 it launches one workgroup that reads nothing: the cost of a
  * launch alone.  sink is device memory of q4_0_reference_read_words(bytes)
  * 32-bit words, 4-byte aligned.  Not a step of the method: the pages weigh

@@ -255,7 +255,7 @@ const char *q4_1_linear_kernel(int64_t M, int64_t K, int64_t N) {
 
 int64_t q4_0_reference_read_words(int64_t bytes) {
     if (bytes < 0 || bytes > (int64_t(1) << 40) || bytes % 16) return 0;
-    return q4::reference_read_workgroups(bytes);
+    return q4::reference_read_sink_words(bytes);
 }
 
 q4_status q4_0_reference_read(const void *src, int64_t bytes, void *sink, void *stream) {

@@ -85,6 +85,7 @@ const char *linear_glu_config_name(int64_t M, int64_t K);
 // Reference streaming read (measurement support): workgroups a read of
 // `bytes` launches, and the launch (sink holds one word per workgroup).
 int64_t reference_read_workgroups(int64_t bytes);
+int64_t reference_read_sink_words(int64_t bytes);   // one word per thread: 256 per workgroup
 hipError_t launch_reference_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s);
 
 // The prefill GEMM's arithmetic alone (measurement support): threads of a

@@ -16,9 +16,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kReadThreads = 256;
 constexpr int kReadPieces = 16;   // 16-byte pieces per thread: 64 KiB per workgroup
 
-// Each workgroup reads its 64 KiB (nontemporal 16-byte loads, all issued
-// before any is used), folds them into one word and writes it to sink, so
-// the loads cannot be removed.
+// Workgroup b reads its 64 KiB (nontemporal 16-byte loads, all issued before
+// any is used; load p of thread t reads 16-byte chunk 4096 b + 256 p + t)
+// and each thread writes the XOR of its 32-bit words to sink, so the loads
+// cannot be removed.  Nothing else follows the loads: no cross-lane fold,
+// LDS or barrier, which would keep the last workgroups of a launch busy
+// after their data has arrived (a serial fold over the threads' words did,
+// by about a microsecond per launch).  The sink adds 1/64 of the bytes read
+// as writes.
 __global__ __launch_bounds__(kReadThreads) void reference_read_kernel(const u32x4 *__restrict__ src, int64_t n16,
                                                                       uint32_t *__restrict__ sink) {
     const int64_t base = static_cast<int64_t>(blockIdx.x) * kReadThreads * kReadPieces + threadIdx.x;
@@ -31,14 +36,7 @@ __global__ __launch_bounds__(kReadThreads) void reference_read_kernel(const u32x
     uint32_t f = 0;
 #pragma unroll
     for (int p = 0; p < kReadPieces; ++p) f ^= v[p].x ^ v[p].y ^ v[p].z ^ v[p].w;
-    __shared__ uint32_t part[kReadThreads];
-    part[threadIdx.x] = f;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t t = 0;
-        for (int i = 0; i < kReadThreads; ++i) t ^= part[i];
-        sink[blockIdx.x] = t;
-    }
+    sink[static_cast<int64_t>(blockIdx.x) * kReadThreads + threadIdx.x] = f;
 }
 
 }  // namespace
@@ -47,6 +45,8 @@ int64_t reference_read_workgroups(int64_t bytes) {
     const int64_t per = static_cast<int64_t>(kReadThreads) * kReadPieces * 16;
     return bytes == 0 ? 1 : (bytes + per - 1) / per;
 }
+
+int64_t reference_read_sink_words(int64_t bytes) { return reference_read_workgroups(bytes) * kReadThreads; }
 
 hipError_t launch_reference_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t s) {
     const int64_t grid = reference_read_workgroups(bytes);

@@ -228,8 +228,8 @@ def test_bench_refuses_more_than_one_gpu():
 
 def test_reference_read_validates_first(L):
     rr, words = L.q4_0_reference_read, L.q4_0_reference_read_words
-    assert words(0) == 1                       # one workgroup: the launch alone
-    assert words(16) == 1 and words(65536) == 1 and words(65552) == 2
+    assert words(0) == 256                     # one workgroup (the launch alone), a word per thread
+    assert words(16) == 256 and words(65536) == 256 and words(65552) == 512
     assert words(-16) == 0 and words(24) == 0 and words(2**40 + 16) == 0
     assert rr(FAKE, 24, FAKE, None) == SHAPE            # not a multiple of 16
     assert rr(FAKE, -16, FAKE, None) == SHAPE

@@ -1,6 +1,7 @@
 """The measurement-support kernels on the GPU: the reference read touches
-every byte it is given (its sink words are the XOR of each 64 KiB piece's
-32-bit words), and the arithmetic-only GEMM loop runs in every mode,
+every byte it is given (sink word 256 b + t is the XOR of the 32-bit words
+of the input's 16-byte chunks 4096 b + 256 p + t, p = 0 .. 15, zero past the
+input), and the arithmetic-only GEMM loop runs in every mode,
 deterministically, with finite results."""
 
 import numpy as np
@@ -14,23 +15,26 @@ from gpu_helpers import DEV, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("nbytes", [16, 65536, 65552, 3 * 65536 + 4096])
+@pytest.mark.parametrize("nbytes", [16, 4096, 16400, 65536, 65552, 3 * 65536 + 4096])
 def test_reference_read_folds_every_word(nbytes):
     rng = np.random.default_rng(nbytes)
     host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
     src = torch.from_numpy(host.view(np.int32).copy()).to(DEV)
     say("reference read", nbytes)
     sink = q4.reference_read(src, nbytes).cpu().numpy().view(np.uint32)
-    words = 65536 // 4
-    want = [np.bitwise_xor.reduce(host[i:i + words]) for i in range(0, host.size, words)]
-    assert np.array_equal(sink, np.array(want, dtype=np.uint32))
+    groups = -(-nbytes // 65536)
+    assert sink.size == int(q4.lib().q4_0_reference_read_words(nbytes)) == 256 * groups
+    chunks = np.zeros((groups * 4096, 4), dtype=np.uint32)      # 16-byte chunks, zero past the input
+    chunks.reshape(-1)[:host.size] = host
+    want = np.bitwise_xor.reduce(chunks.reshape(groups, 16, 256, 4), axis=(1, 3)).reshape(-1)
+    assert np.array_equal(sink, want)
 
 
 def test_reference_read_of_nothing_is_one_launch():
     src = torch.zeros(16, dtype=torch.uint8, device=DEV)
     sink = q4.reference_read(src, 0)
     torch.cuda.synchronize()
-    assert sink.numel() == 1 and int(sink[0]) == 0
+    assert sink.numel() == 256 and int(sink.abs().sum()) == 0
 
 
 @pytest.mark.parametrize("mode", [0, 1, 2, 3])
