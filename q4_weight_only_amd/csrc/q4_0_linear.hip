@@ -427,7 +427,6 @@ void gemv_kernel(const LinearArgs a) {
     static_assert(MROWS >= 1 && MROWS <= 16, "one 16-row m-tile");
     static_assert(!(GLU && ASYM), "no gated launch of the asymmetric layout");
     constexpr int REGS = MROWS < 4 ? MROWS : 4;
-    constexpr int kThreads = 64 * WK;
     extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
     const int lane = threadIdx.x & 63;
     const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -440,14 +439,13 @@ void gemv_kernel(const LinearArgs a) {
     const int half = GLU ? static_cast<int>(blockIdx.x) & 1 : 0;
     const int KT = a.KT;
     const int mrows = a.M < MROWS ? a.M : MROWS;
-    const int row_bytes = x_row_bytes(KT);
 
-    // x chunks (16 bytes) of the staged tile: KT <= NS * WK super-tiles of
-    // 16 chunks per row, so a thread owns at most kXPer of them
-    constexpr int kXPer = (MROWS * NS * WK * (kTileK / 8) + kThreads - 1) / kThreads;
-    const int chunks_per_row = KT * (kTileK / 8);
-    const int xtotal = mrows * chunks_per_row;
-
+    // x: each wave stages only the chunks (16 bytes) its own super-tiles
+    // read, [row][stage][chunk], into an LDS region of its own, so no wave
+    // waits for another's x; lane L takes chunks L, L + 64, ...
+    constexpr int kWaveChunks = MROWS * NS * (kTileK / 8);
+    constexpr int kXPer = (kWaveChunks + 63) / 64;
+    uint8_t *const xw = xs + wk * (kWaveChunks * 16);
     // weights: past the segment's end the last tile is read (its outputs are
     // never stored)
     const int rt = rt0 < sg.RT ? rt0 : sg.RT - 1;
@@ -477,16 +475,12 @@ void gemv_kernel(const LinearArgs a) {
     const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.x), 0, mrows * a.K * 2, kBufferRsrcWord3);
     u32x4 xv[kXPer];
-    int xdst[kXPer];
 #pragma unroll
     for (int q = 0; q < kXPer; ++q) {
-        const int c = threadIdx.x + q * kThreads;
-        // the row index without an integer division at one and two rows
-        const int m = MROWS == 1 ? 0 : MROWS == 2 ? (c >= chunks_per_row ? 1 : 0) : c / chunks_per_row;
-        const int kc = c - m * chunks_per_row;
-        const bool in = c < xtotal && kc * 8 < a.K;
-        // a thread without a chunk stores its zeros to the pad slot after the tile
-        xdst[q] = c < xtotal ? m * row_bytes + kc * 16 : mrows * row_bytes;
+        const int c = lane + 64 * q;                       // [row][stage][chunk] of this wave
+        const int m = c / (NS * 16), st = (c / 16) % NS, cc = c % 16;
+        const int kt = wk + st * WK, kc = kt * 16 + cc;    // 16-byte chunk of the row
+        const bool in = c < kWaveChunks && m < mrows && kt < KT && kc * 8 < a.K;
         xv[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                               xrsrc, in ? (m * a.K + kc * 8) * 2 : kOutOfRange, 0, 0));
     }
@@ -517,13 +511,18 @@ void gemv_kernel(const LinearArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);   // stages go out in order
     }
-    // 3. x into LDS (waits for the x loads only), one barrier
+    // 3. this wave's x into its LDS region (waits for the x loads only);
+    //    the region is the wave's alone, so a wave-scope fence stands in for
+    //    a workgroup barrier
 #pragma unroll
-    for (int q = 0; q < kXPer; ++q) *reinterpret_cast<u32x4 *>(xs + xdst[q]) = xv[q];
-    __syncthreads();
+    for (int q = 0; q < kXPer; ++q)
+        if (lane + 64 * q < kWaveChunks) *reinterpret_cast<u32x4 *>(xw + (lane + 64 * q) * 16) = xv[q];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // 4. stage j's MFMAs wait for stage j's weights only
-    const int a_off = (nl < mrows ? nl : mrows - 1) * row_bytes + g * 16;
+    const int a_off = (nl < mrows ? nl : mrows - 1) * (NS * 256) + g * 16;
     floatx4 acc = (floatx4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
@@ -534,8 +533,7 @@ void gemv_kernel(const LinearArgs a) {
         if constexpr (ASYM) moj = live ? mo[j] : (u32x2){0u, 0u};
 #pragma unroll
         for (int i = 0; i < kTileBlocks; ++i) {
-            const int b = ktj[j] * kTileBlocks + i;
-            const bf16x8 A = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xs + a_off + b * kQK * 2));
+            const bf16x8 A = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(xw + a_off + j * 256 + i * 64));
             const bf16x8 B = ASYM ? decode_piece_u(piece_of(nib[j], i)) : decode_piece(piece_of(nib[j], i));
             const float d = scale_of(scj, i);
             const floatx4 D = mfma_block(A, B);
@@ -1423,8 +1421,9 @@ template <int MROWS, int WK, int WPE, bool GLU, int NSMAX, bool ASYM = false>
 hipError_t run_gemv(LinearArgs a, hipStream_t s) {
     static_assert(NSMAX >= 1 && NSMAX <= kGemvMaxStages, "stage count");
     const int tiles = assign_tiles<GLU>(a, 1) * (GLU ? 2 : 1);   // gated: two 8-row halves per tile
-    const uint32_t lds = static_cast<uint32_t>(skinny_x_bytes(a.M, a.K, MROWS)) + 16;   // + the pad slot
-    switch (gemv_stages(a, WK)) {
+    const int ns = gemv_stages(a, WK);
+    const uint32_t lds = static_cast<uint32_t>(WK * MROWS * ns * 256);   // each wave's x chunks
+    switch (ns) {
         case 1: return launch_gemv_ns<MROWS, WK, 1, WPE, GLU, ASYM>(a, tiles, lds, s);
         case 2: if constexpr (NSMAX >= 2) return launch_gemv_ns<MROWS, WK, 2, WPE, GLU, ASYM>(a, tiles, lds, s); break;
         case 3: if constexpr (NSMAX >= 3) return launch_gemv_ns<MROWS, WK, 3, WPE, GLU, ASYM>(a, tiles, lds, s); break;
