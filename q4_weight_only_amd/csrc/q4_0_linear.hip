@@ -1500,7 +1500,7 @@ bool take_launch_events(hipEvent_t &start, hipEvent_t &stop) {
 // results of an output in the same order, so the choice never changes a
 // result.
 namespace {
-enum class Cfg { G1, G1K, G2, G2K, G4, G4K, M1Stream, M1Long, M2Long, M4Long, M16, M16Long, M32, M32Split, M32Split2,
+enum class Cfg { G1, G1K, G2, G2K, G4, G4K, G1L, G2L, M1Stream, M1Long, M2Long, M4Long, M16, M16Long, M32, M32Split, M32Split2,
                  M64, M64Split,
                  Gemm64, Gemm128, Gemm128W, Gemm96W };
 
@@ -1508,15 +1508,17 @@ enum class Cfg { G1, G1K, G2, G2K, G4, G4K, M1Stream, M1Long, M2Long, M4Long, M1
 // GEMM split at 2048 rows.
 Cfg pick_mk(int64_t M, int64_t K) {
     // up to 4 rows: the decode kernel with every stage in flight for K up to
-    // 4096 (3 or 4 stages per wave); longer rows keep the 2-stage refill of
-    // the K-split kernel, which measured faster there (down 9216 -> 3072:
-    // 7.6 against 8.2 us with five stages in flight)
+    // 4096 (3 or 4 stages per wave)
     if (M <= 4 && K <= 4096) {
         const bool k3 = K <= 3072;
         if (M == 1) return k3 ? Cfg::G1 : Cfg::G1K;
         if (M == 2) return k3 ? Cfg::G2 : Cfg::G2K;
         return k3 ? Cfg::G4 : Cfg::G4K;
     }
+    // one or two rows up to K = 9216: 12 K-slices of up to 6 stages, all in
+    // flight (down 9216 -> 3072: 7.0-7.1 us against 7.2-7.6 with the 2-stage
+    // refill of the K-split kernel, and 16 K-slices of 5 stages between)
+    if (M <= 2 && K <= 12 * kGemvMaxStages * kTileK) return M == 1 ? Cfg::G1L : Cfg::G2L;
     if (M == 1) return Cfg::M1Long;
     if (M == 2) return Cfg::M2Long;
     if (M <= 4) return Cfg::M4Long;
@@ -1593,7 +1595,7 @@ const char *gemv_name(int mrows, int wk, int ns, int wpe, bool glu, bool asym = 
     static const std::vector<std::string> table = [] {
         std::vector<std::string> t;
         for (int m : {1, 2, 4})
-            for (int w : {4, 8, 16})
+            for (int w : {4, 8, 12, 16})
                 for (int n = 1; n <= kGemvMaxStages; ++n)
                     for (int e : {0, 6})
                         for (int gl : {0, 1})
@@ -1603,9 +1605,9 @@ const char *gemv_name(int mrows, int wk, int ns, int wpe, bool glu, bool asym = 
                                             (gl ? "true" : "false") + (as ? ", true>" : ">"));
         return t;
     }();
-    const int mi = mrows == 1 ? 0 : mrows == 2 ? 1 : 2, wi = wk == 4 ? 0 : wk == 8 ? 1 : 2;
+    const int mi = mrows == 1 ? 0 : mrows == 2 ? 1 : 2, wi = wk == 4 ? 0 : wk == 8 ? 1 : wk == 12 ? 2 : 3;
     if (ns < 1 || ns > kGemvMaxStages) return "";
-    return table[(((((mi * 3 + wi) * kGemvMaxStages + ns - 1) * 2 + (wpe ? 1 : 0)) * 2 + (glu ? 1 : 0)) * 2 +
+    return table[(((((mi * 4 + wi) * kGemvMaxStages + ns - 1) * 2 + (wpe ? 1 : 0)) * 2 + (glu ? 1 : 0)) * 2 +
                   (asym ? 1 : 0))].c_str();
 }
 
@@ -1620,11 +1622,14 @@ GemvCfg gemv_cfg(Cfg c) {
         case Cfg::G2: return {2, 8, 0};
         case Cfg::G2K: return {2, 8, 0};
         case Cfg::G4: return {4, 8, 0};
+        case Cfg::G1L: return {1, 12, 0};
+        case Cfg::G2L: return {2, 12, 0};
         default: return {4, 16, 0};   // G4K
     }
 }
 bool is_gemv(Cfg c) {
-    return c == Cfg::G1 || c == Cfg::G1K || c == Cfg::G2 || c == Cfg::G2K || c == Cfg::G4 || c == Cfg::G4K;
+    return c == Cfg::G1 || c == Cfg::G1K || c == Cfg::G2 || c == Cfg::G2K || c == Cfg::G4 || c == Cfg::G4K ||
+           c == Cfg::G1L || c == Cfg::G2L;
 }
 
 const char *linear_config_name(const LinearArgs &a) {
@@ -1661,6 +1666,8 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
         case Cfg::G2K: return run_gemv<2, 8, 0, false, 4>(a, s);
         case Cfg::G4: return run_gemv<4, 8, 0, false, 3>(a, s);
         case Cfg::G4K: return run_gemv<4, 16, 0, false, 2>(a, s);
+        case Cfg::G1L: return run_gemv<1, 12, 0, false, 6>(a, s);
+        case Cfg::G2L: return run_gemv<2, 12, 0, false, 6>(a, s);
         case Cfg::M1Long: return run_skinny<1, 1, 16, 2, 0>(a, s);
         case Cfg::M2Long: return run_skinny<2, 1, 16, 2, 0>(a, s);
         case Cfg::M4Long: return run_skinny<4, 1, 16, 2, 0>(a, s);
@@ -1714,6 +1721,8 @@ hipError_t launch_linear_glu(LinearArgs a, hipStream_t s) {
         case Cfg::G2K: return run_gemv<2, 8, 0, true, 4>(a, s);
         case Cfg::G4: return run_gemv<4, 8, 0, true, 3>(a, s);
         case Cfg::G4K: return run_gemv<4, 16, 0, true, 2>(a, s);
+        case Cfg::G1L: return run_gemv<1, 12, 0, true, 6>(a, s);
+        case Cfg::G2L: return run_gemv<2, 12, 0, true, 6>(a, s);
         case Cfg::M1Long: return run_skinny<1, 1, 8, 3, 0, true>(a, s);
         case Cfg::M2Long: return run_skinny<2, 1, 8, 3, 0, true>(a, s);
         case Cfg::M4Long: return run_skinny<4, 1, 8, 3, 0, true>(a, s);

@@ -38,6 +38,21 @@ def test_linear_parity_grid(m, n, k):
     _run_and_check(w, x, f"M={m} N={n} K={k}")
 
 
+# one and two rows on long rows: 12 K-slices of up to 6 stages (K 4097-9216;
+# where 12 does not divide the super-tiles some stages lie past K, and a last
+# super-tile may be partial), the K-split kernel beyond 9216 and at 3-4 rows
+LONG_NKS = [(40, 4128), (48, 5152), (24, 9184), (72, 9216), (16, 9248)]
+
+
+@pytest.mark.parametrize("m", [1, 2, 3])
+@pytest.mark.parametrize("n,k", LONG_NKS)
+def test_linear_long_rows(m, n, k):
+    w = inputs.weights_f32((n, k), seed=23, tags=(n, k))
+    x = inputs.activations_bf16((m, k), seed=23, tags=(m, k))
+    say("long rows", q4.linear_kernel(m, k, [n]))
+    _run_and_check(w, x, f"M={m} N={n} K={k}")
+
+
 @pytest.mark.parametrize("m", [1, 2, 4, 16, 32, 64])
 def test_all_codes_eight_give_zero(m):
     n, k = 64, 512
