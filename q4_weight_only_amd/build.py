@@ -36,6 +36,9 @@ COMMON_FLAGS = [
     # MFMA results in VGPRs: the per-block fp32 rescale reads them directly
     # instead of copying each one out of an AGPR first.
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # Up to 12 leading scalar kernel arguments arrive preloaded in SGPRs, so a
+    # decode launch's first loads do not wait on a fetch of its arguments.
+    "-mllvm", "-amdgpu-kernarg-preload-count=12",
     "-Wall",
     "-Wextra",
     "-Wno-unused-command-line-argument",

@@ -423,7 +423,9 @@ constexpr int kNonTemporal = 2;           // cache-policy bit of a buffer load: 
 // block's sum S of x, and each block adds d * D + m * S (no final * 16).
 template <int MROWS, int WK, int NS, int WPE, bool GLU, bool ASYM = false>
 __global__ __launch_bounds__(64 * WK) __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, 8)))
-void gemv_kernel(const LinearArgs a) {
+void gemv_kernel(const uint16_t *__restrict__ ax, const int aM, const int aK, const int aKT, const int anseg,
+                 const int tb1, const int tb2, const int tb3, const int tb4, const int tb5, const int tb6,
+                 const int tb7, const LinearArgs a) {
     static_assert(MROWS >= 1 && MROWS <= 16, "one 16-row m-tile");
     static_assert(!(GLU && ASYM), "no gated launch of the asymmetric layout");
     constexpr int REGS = MROWS < 4 ? MROWS : 4;
@@ -432,20 +434,37 @@ void gemv_kernel(const LinearArgs a) {
     const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nl = lane & 15, g = lane >> 4;
 
-    const int s = GLU ? 0 : find_segment(a, blockIdx.x);
+    // the segment from the start tiles passed as scalar arguments: with them
+    // preloaded into SGPRs the segment is known without a load, and only its
+    // pointers are fetched before the weight loads
+    int s = 0;
+    if constexpr (!GLU) {
+        const int tbs[kMaxSegments - 1] = {tb1, tb2, tb3, tb4, tb5, tb6, tb7};
+#pragma unroll
+        for (int t = 1; t < kMaxSegments; ++t)
+            if (t < anseg && static_cast<int>(blockIdx.x) >= tbs[t - 1]) s = t;
+    }
     const Segment sg = a.seg[s];
-    // plain: 16-row tile rt0; gated: tile rt0, rows 8 h .. 8 h + 7 of it
-    const int rt0 = GLU ? static_cast<int>(blockIdx.x) >> 1 : static_cast<int>(blockIdx.x) - sg.tile_begin;
-    const int half = GLU ? static_cast<int>(blockIdx.x) & 1 : 0;
-    const int KT = a.KT;
-    const int mrows = a.M < MROWS ? a.M : MROWS;
+    // plain: 16-row tile rt0; gated: tile rt0, rows 8 h .. 8 h + 7 of it.
+    // Gated workgroups come in groups of 16: b and b + 8 take the two halves
+    // of one tile, so that under round-robin dispatch over the 8 XCDs both
+    // halves of each 256-byte code piece are fetched through one XCD at about
+    // the same time (adjacent b would split every piece across two XCDs)
+    const int b = static_cast<int>(blockIdx.x);
+    const int rt0 = GLU ? ((b >> 4) << 3) + (b & 7) : b - sg.tile_begin;
+    const int half = GLU ? (b >> 3) & 1 : 0;
+    const int KT = aKT;
+    const int mrows = aM < MROWS ? aM : MROWS;
 
     // x: each wave stages only the chunks (16 bytes) its own super-tiles
     // read, [row][stage][chunk], into an LDS region of its own, so no wave
     // waits for another's x; lane L takes chunks L, L + 64, ...
     constexpr int kWaveChunks = MROWS * NS * (kTileK / 8);
     constexpr int kXPer = (kWaveChunks + 63) / 64;
-    uint8_t *const xw = xs + wk * (kWaveChunks * 16);
+    // with a pad slot for each lane past the chunks, so that every lane stores
+    // (a conditional store lets the compiler sink the x loads below the
+    // weight loads, and the first stage then waits for all of them)
+    uint8_t *const xw = xs + wk * (kXPer * 64 * 16);
     // weights: past the segment's end the last tile is read (its outputs are
     // never stored)
     const int rt = rt0 < sg.RT ? rt0 : sg.RT - 1;
@@ -473,16 +492,16 @@ void gemv_kernel(const LinearArgs a) {
     // 1. x first: every chunk of this thread, zero past K (a chunk past the
     //    row's K, or a thread without a chunk, reads beyond the resource)
     const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(a.x), 0, mrows * a.K * 2, kBufferRsrcWord3);
+        const_cast<uint16_t *>(ax), 0, mrows * aK * 2, kBufferRsrcWord3);
     u32x4 xv[kXPer];
 #pragma unroll
     for (int q = 0; q < kXPer; ++q) {
         const int c = lane + 64 * q;                       // [row][stage][chunk] of this wave
         const int m = c / (NS * 16), st = (c / 16) % NS, cc = c % 16;
         const int kt = wk + st * WK, kc = kt * 16 + cc;    // 16-byte chunk of the row
-        const bool in = c < kWaveChunks && m < mrows && kt < KT && kc * 8 < a.K;
+        const bool in = c < kWaveChunks && m < mrows && kt < KT && kc * 8 < aK;
         xv[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              xrsrc, in ? (m * a.K + kc * 8) * 2 : kOutOfRange, 0, 0));
+                                              xrsrc, in ? (m * aK + kc * 8) * 2 : kOutOfRange, 0, 0));
     }
     __builtin_amdgcn_sched_barrier(0);   // keep the x loads ahead of the weights
 
@@ -516,7 +535,7 @@ void gemv_kernel(const LinearArgs a) {
     //    a workgroup barrier
 #pragma unroll
     for (int q = 0; q < kXPer; ++q)
-        if (lane + 64 * q < kWaveChunks) *reinterpret_cast<u32x4 *>(xw + (lane + 64 * q) * 16) = xv[q];
+        *reinterpret_cast<u32x4 *>(xw + (lane + 64 * q) * 16) = xv[q];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -571,7 +590,7 @@ void gemv_kernel(const LinearArgs a) {
 #pragma unroll
         for (int r = 0; r < REGS; ++r) {
             const int m = 4 * g + r;
-            if (m < a.M) store_out(a, sg, static_cast<int64_t>(m) * sg.N + n, silu_f32(acc[r] * 16.0f) * (u[r] * 16.0f));
+            if (m < aM) store_out(a, sg, static_cast<int64_t>(m) * sg.N + n, silu_f32(acc[r] * 16.0f) * (u[r] * 16.0f));
         }
     } else {
         const int n = rt0 * 16 + nl;
@@ -579,7 +598,7 @@ void gemv_kernel(const LinearArgs a) {
 #pragma unroll
         for (int r = 0; r < REGS; ++r) {
             const int m = 4 * g + r;
-            if (m < a.M) sg.y[static_cast<int64_t>(m) * sg.N + n] = ASYM ? acc[r] : acc[r] * 16.0f;
+            if (m < aM) sg.y[static_cast<int64_t>(m) * sg.N + n] = ASYM ? acc[r] : acc[r] * 16.0f;
         }
     }
 }
@@ -1259,16 +1278,16 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
 thread_local hipEvent_t t_start_event = nullptr;
 thread_local hipEvent_t t_stop_event = nullptr;
 
-template <typename Kernel>
+template <typename Kernel, typename... Args>
 hipError_t launch_kernel(Kernel kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
-                         const LinearArgs &a) {
+                         const Args &...a) {
     if (t_start_event || t_stop_event) {
         hipEvent_t start = t_start_event, stop = t_stop_event;
         t_start_event = t_stop_event = nullptr;
         // records the events at the kernel's own start and end
-        hipExtLaunchKernelGGL(kernel, grid, block, lds, s, start, stop, 0, a);
+        hipExtLaunchKernelGGL(kernel, grid, block, lds, s, start, stop, 0, a...);
     } else {
-        hipLaunchKernelGGL(kernel, grid, block, lds, s, a);
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, a...);
     }
     return hipGetLastError();
 }
@@ -1412,7 +1431,11 @@ hipError_t launch_gemv_ns(const LinearArgs &a, int tiles, uint32_t lds, hipStrea
     static std::atomic<uint64_t> lds_allowed{0};
     const hipError_t e = allow_dynamic_lds(kernel, lds_allowed);
     if (e != hipSuccess) return e;
-    return launch_kernel(kernel, dim3(tiles), dim3(64 * WK), lds, s, a);
+    // x, the sizes and the segments' start tiles go ahead of the segment table
+    // as scalar arguments (preloaded into SGPRs where the firmware supports it)
+    return launch_kernel(kernel, dim3(tiles), dim3(64 * WK), lds, s, a.x, a.M, a.K, a.KT, a.nseg, a.seg[1].tile_begin,
+                         a.seg[2].tile_begin, a.seg[3].tile_begin, a.seg[4].tile_begin, a.seg[5].tile_begin,
+                         a.seg[6].tile_begin, a.seg[7].tile_begin, a);
 }
 
 // NSMAX: the most stages the dispatch can ask of this configuration (only
@@ -1420,9 +1443,12 @@ hipError_t launch_gemv_ns(const LinearArgs &a, int tiles, uint32_t lds, hipStrea
 template <int MROWS, int WK, int WPE, bool GLU, int NSMAX, bool ASYM = false>
 hipError_t run_gemv(LinearArgs a, hipStream_t s) {
     static_assert(NSMAX >= 1 && NSMAX <= kGemvMaxStages, "stage count");
-    const int tiles = assign_tiles<GLU>(a, 1) * (GLU ? 2 : 1);   // gated: two 8-row halves per tile
+    // gated: two 8-row halves per tile, in groups of 8 tiles (the groups past
+    // the last tile read it again and store nothing)
+    const int tiles = GLU ? (assign_tiles<GLU>(a, 1) + 7) / 8 * 16 : assign_tiles<GLU>(a, 1);
     const int ns = gemv_stages(a, WK);
-    const uint32_t lds = static_cast<uint32_t>(WK * MROWS * ns * 256);   // each wave's x chunks
+    // each wave's x chunks, rounded up to whole 64-lane stores
+    const uint32_t lds = static_cast<uint32_t>(WK * ((MROWS * ns * 16 + 63) / 64) * 64 * 16);
     switch (ns) {
         case 1: return launch_gemv_ns<MROWS, WK, 1, WPE, GLU, ASYM>(a, tiles, lds, s);
         case 2: if constexpr (NSMAX >= 2) return launch_gemv_ns<MROWS, WK, 2, WPE, GLU, ASYM>(a, tiles, lds, s); break;
