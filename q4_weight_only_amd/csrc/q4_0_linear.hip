@@ -1762,15 +1762,17 @@ hipError_t launch_linear_glu(LinearArgs a, hipStream_t s) {
 }
 
 // The asymmetric layout (one segment): up to 4 rows and K up to 12288 the
-// decode kernel (8 K-slices up to K = 3072 at one row and 4096 at two, 16
-// beyond), otherwise the GEMM (32- or 64-row tiles up to 64 rows, the tile
+// decode kernel (8 K-slices up to K = 3072 at one row and 4096 at two; 12 of
+// up to 6 stages from there to K = 9216 at one and two rows, which took the
+// 9216 -> 3072 launch from 6.9-7.0 to 6.5 us at one row; 16 otherwise),
+// otherwise the GEMM (32- or 64-row tiles up to 64 rows, the tile
 // model above that).
 namespace {
-enum class Q41 { G1, G1K, G2, G2K, G4, Gemm32, Gemm64r, Gemm64, Gemm128, Gemm128W };
+enum class Q41 { G1, G1K, G2, G2K, G4, G1L, G2L, Gemm32, Gemm64r, Gemm64, Gemm128, Gemm128W };
 Q41 pick_q41(const LinearArgs &a) {
     if (a.M <= 4 && a.KT <= 96) {
-        if (a.M == 1) return a.KT <= 24 ? Q41::G1 : Q41::G1K;
-        if (a.M == 2) return a.KT <= 32 ? Q41::G2 : Q41::G2K;
+        if (a.M == 1) return a.KT <= 24 ? Q41::G1 : a.KT <= 32 ? Q41::G1K : a.KT <= 72 ? Q41::G1L : Q41::G1K;
+        if (a.M == 2) return a.KT <= 32 ? Q41::G2 : a.KT <= 72 ? Q41::G2L : Q41::G2K;
         return Q41::G4;
     }
     if (a.M <= 32) return Q41::Gemm32;
@@ -1792,6 +1794,8 @@ const char *linear_q41_config_name(const LinearArgs &a) {
         case Q41::G2: return gemv_name(2, 8, (a.KT + 7) / 8, 0, false, true);
         case Q41::G2K: return gemv_name(2, 16, ns16, 0, false, true);
         case Q41::G4: return gemv_name(4, 16, ns16, 0, false, true);
+        case Q41::G1L: return gemv_name(1, 12, (a.KT + 11) / 12, 0, false, true);
+        case Q41::G2L: return gemv_name(2, 12, (a.KT + 11) / 12, 0, false, true);
         case Q41::Gemm32: return "gemm3_kernel<2, 1, 1, 8, 0, 8, false, true>";
         case Q41::Gemm64r: return "gemm3_kernel<4, 1, 1, 8, 0, 8, false, true>";
         case Q41::Gemm64: return "gemm3_kernel<4, 1, 1, 8, 0, 8, false, true>";
@@ -1807,6 +1811,8 @@ hipError_t launch_linear_q41(LinearArgs a, hipStream_t s) {
         case Q41::G2: return run_gemv<2, 8, 0, false, 4, true>(a, s);
         case Q41::G2K: return run_gemv<2, 16, 0, false, 6, true>(a, s);
         case Q41::G4: return run_gemv<4, 16, 0, false, 6, true>(a, s);
+        case Q41::G1L: return run_gemv<1, 12, 0, false, 6, true>(a, s);
+        case Q41::G2L: return run_gemv<2, 12, 0, false, 6, true>(a, s);
         case Q41::Gemm32: return run_gemm3<2, 1, 1, 8, 0, 8, false, true>(a, s);
         case Q41::Gemm64r: return run_gemm3<4, 1, 1, 8, 0, 8, false, true>(a, s);
         case Q41::Gemm64: return run_gemm3<4, 1, 1, 8, 0, 8, false, true>(a, s);

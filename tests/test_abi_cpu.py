@@ -274,6 +274,9 @@ def test_q41_entry_points_validate_first(L):
     kn = L.q4_1_linear_kernel
     assert kn(0, 64, 16) == b""
     assert kn(1, 3072, 4096) == b"gemv_kernel<1, 8, 3, 6, false, true>"
-    assert kn(1, 9216, 3072) == b"gemv_kernel<1, 16, 5, 0, false, true>"
+    assert kn(1, 9216, 3072) == b"gemv_kernel<1, 12, 6, 0, false, true>"
+    assert kn(2, 5120, 3072) == b"gemv_kernel<2, 12, 4, 0, false, true>"
+    assert kn(1, 4096, 3072) == b"gemv_kernel<1, 16, 2, 0, false, true>"
+    assert kn(1, 12288, 3072) == b"gemv_kernel<1, 16, 6, 0, false, true>"   # past 12 x 6 stages
     assert kn(3, 20480, 64) == b"gemm3_kernel<2, 1, 1, 8, 0, 8, false, true>"   # K past the decode kernel's reach
     assert kn(40, 3072, 3072) == b"gemm3_kernel<4, 1, 1, 8, 0, 8, false, true>"

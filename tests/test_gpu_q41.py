@@ -49,6 +49,8 @@ def test_pack_and_dequant_bit_exact(n, k):
 
 GRID = [(m, n, k) for m in (1, 2, 3, 4, 5, 17, 33, 64, 65, 130, 300) for n, k in ((64, 128), (40, 384), (200, 1280))]
 GRID += [(1, 48, 9216), (2, 48, 12288), (4, 24, 4096), (3, 32, 20480), (1, 17, 32), (1505, 72, 640)]
+# one and two rows at K 4097-9216: 12 K-slices, with stages past K (5152) and a partial last super-tile (9184)
+GRID += [(1, 40, 5152), (2, 40, 5152), (1, 24, 9184), (2, 24, 9184)]
 
 
 @pytest.mark.parametrize("m,n,k", GRID)
