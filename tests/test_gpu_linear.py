@@ -150,6 +150,28 @@ def test_multi_equals_separate_calls_bitwise(m):
         assert_within_bound(y.cpu().numpy(), O.linear(xb, b, w.shape[0], k), O.error_bound(xb, b, w.shape[0], k))
 
 
+@pytest.mark.parametrize("m,k", [(1, 3072), (2, 4096), (1, 5120), (3, 384), (2, 9216), (40, 384)])
+def test_eight_segments(m, k):
+    """The most segments a launch takes (8, ragged and of different lengths):
+    every segment's work tiles are found from the start tiles of the others,
+    which the decode kernel receives as separate scalar arguments.  Each output
+    against the oracle, and bit for bit against a separate launch where the
+    two pick the same kernel (the decode sizes: the choice follows M and K)."""
+    ns = (16, 40, 8, 136, 24, 1, 72, 33)
+    ws = [inputs.weights_f32((n, k), seed=10, tags=(i, k)) for i, n in enumerate(ns)]
+    pws = [device_weight_from_f32(w)[0] for w in ws]
+    xb = inputs.activations_bf16((m, k), seed=10, tags=(m, k))
+    x = to_dev_x(xb)
+    say("eight segments", m, k, q4.linear_kernel(m, k, list(ns)))
+    ys = q4.linear_multi(x, pws)
+    for si, (w, pw, y) in enumerate(zip(ws, pws, ys)):
+        b = O.quantize(w)
+        assert_within_bound(y.cpu().numpy(), O.linear(xb, b, w.shape[0], k), O.error_bound(xb, b, w.shape[0], k),
+                            f"M={m} K={k} segment {si}")
+        if m <= 4:
+            assert torch.equal(y, q4.linear(x, pw)), f"M={m} K={k} segment {si}: fused and separate differ"
+
+
 @pytest.mark.parametrize("m", [1, 2, 32, 129])
 def test_bitwise_deterministic(m):
     n, k = 512, 1024
