@@ -14,10 +14,11 @@
 // the dequantization split so that no weight is ever rounded.
 //
 // Kernels.
-//   gemv_kernel    (M <= 4, K <= 4096: the decode step's QKV, O and gate/up):
-//                  a workgroup owns one 16-row weight tile and all M rows, its
-//                  WK waves split K; each wave issues x and then every one of
-//                  its weight stages at once and consumes them as they land.
+//   gemv_kernel    (M <= 4 with K <= 4096, and M <= 2 with K <= 9216: every
+//                  launch of the decode step): a workgroup owns one 16-row
+//                  weight tile and all M rows, its WK waves split K; each wave
+//                  issues its own x chunks and then every one of its weight
+//                  stages at once, and consumes them as they land.
 //   skinny_kernel  (other M <= 16, and 17-64 rows when the weights are
 //                  short): the same work split with a P-deep refill of each
 //                  wave's stages; x from LDS (staged once) or global memory.
@@ -1418,10 +1419,11 @@ hipError_t run_skinny(LinearArgs a, hipStream_t s) {
     return launch_kernel(skinny_kernel<MROWS, NT, WK, P, false, WPE, GLU>, dim3(tiles), dim3(kThreads), 0, s, a);
 }
 
-// The decode kernel with x staged in LDS and all NS = ceil(KT / WK) weight
-// stages of a wave in flight at once: up to kGemvMaxStages stages.  The
-// dispatch takes it for M <= 4 and K <= 4096 only, where x takes at most
-// 4 rows of 8 KiB of LDS; the launcher instantiates one kernel per NS.
+// The decode kernel with all NS = ceil(KT / WK) weight stages of a wave in
+// flight at once: up to kGemvMaxStages stages, so the dispatch takes it for
+// KT <= 6 WK (K <= 4096 at up to 4 rows, K <= 9216 with 12 K-slices at one and
+// two rows).  Each wave stages its own x chunks (at most 4 rows x 6 stages x
+// 256 bytes); the launcher instantiates one kernel per NS.
 constexpr int kGemvMaxStages = 6;
 inline int gemv_stages(const LinearArgs &a, int wk) { return (a.KT + wk - 1) / wk; }
 
