@@ -14,8 +14,8 @@
 // the dequantization split so that no weight is ever rounded.
 //
 // Kernels.
-//   gemv_kernel    (M <= 4 with K <= 4096, and M <= 2 with K <= 9216: every
-//                  launch of the decode step): a workgroup owns one 16-row
+//   gemv_kernel    (M <= 4 with K <= 9216: every launch of the decode step;
+//                  gated launches of 3-4 rows only to K = 4096): a workgroup owns one 16-row
 //                  weight tile and all M rows, its WK waves split K; each wave
 //                  issues its own x chunks and then every one of its weight
 //                  stages at once, and consumes them as they land.
@@ -1421,8 +1421,7 @@ hipError_t run_skinny(LinearArgs a, hipStream_t s) {
 
 // The decode kernel with all NS = ceil(KT / WK) weight stages of a wave in
 // flight at once: up to kGemvMaxStages stages, so the dispatch takes it for
-// KT <= 6 WK (K <= 4096 at up to 4 rows, K <= 9216 with 12 K-slices at one and
-// two rows).  Each wave stages its own x chunks (at most 4 rows x 6 stages x
+// KT <= 6 WK (K <= 4096 with 8 or 16 K-slices, K <= 9216 with 12).  Each wave stages its own x chunks (at most 4 rows x 6 stages x
 // 256 bytes); the launcher instantiates one kernel per NS.
 constexpr int kGemvMaxStages = 6;
 inline int gemv_stages(const LinearArgs &a, int wk) { return (a.KT + wk - 1) / wk; }
@@ -1528,7 +1527,7 @@ bool take_launch_events(hipEvent_t &start, hipEvent_t &stop) {
 // results of an output in the same order, so the choice never changes a
 // result.
 namespace {
-enum class Cfg { G1, G1K, G2, G2K, G4, G4K, G1L, G2L, M1Stream, M1Long, M2Long, M4Long, M16, M16Long, M32, M32Split, M32Split2,
+enum class Cfg { G1, G1K, G2, G2K, G4, G4K, G1L, G2L, G4L, M1Stream, M1Long, M2Long, M4Long, M16, M16Long, M32, M32Split, M32Split2,
                  M64, M64Split,
                  Gemm64, Gemm128, Gemm128W, Gemm96W };
 
@@ -1543,10 +1542,10 @@ Cfg pick_mk(int64_t M, int64_t K) {
         if (M == 2) return k3 ? Cfg::G2 : Cfg::G2K;
         return k3 ? Cfg::G4 : Cfg::G4K;
     }
-    // one or two rows up to K = 9216: 12 K-slices of up to 6 stages, all in
-    // flight (down 9216 -> 3072: 7.0-7.1 us against 7.2-7.6 with the 2-stage
-    // refill of the K-split kernel, and 16 K-slices of 5 stages between)
-    if (M <= 2 && K <= 12 * kGemvMaxStages * kTileK) return M == 1 ? Cfg::G1L : Cfg::G2L;
+    // up to K = 9216: 12 K-slices of up to 6 stages, all in flight (down
+    // 9216 -> 3072: 7.0-7.1 us against 7.2-7.6 with the 2-stage refill of the
+    // K-split kernel at one row, 7.4-7.5 against 8.2-8.8 at three and four)
+    if (M <= 4 && K <= 12 * kGemvMaxStages * kTileK) return M == 1 ? Cfg::G1L : M == 2 ? Cfg::G2L : Cfg::G4L;
     if (M == 1) return Cfg::M1Long;
     if (M == 2) return Cfg::M2Long;
     if (M <= 4) return Cfg::M4Long;
@@ -1652,12 +1651,13 @@ GemvCfg gemv_cfg(Cfg c) {
         case Cfg::G4: return {4, 8, 0};
         case Cfg::G1L: return {1, 12, 0};
         case Cfg::G2L: return {2, 12, 0};
+        case Cfg::G4L: return {4, 12, 0};
         default: return {4, 16, 0};   // G4K
     }
 }
 bool is_gemv(Cfg c) {
     return c == Cfg::G1 || c == Cfg::G1K || c == Cfg::G2 || c == Cfg::G2K || c == Cfg::G4 || c == Cfg::G4K ||
-           c == Cfg::G1L || c == Cfg::G2L;
+           c == Cfg::G1L || c == Cfg::G2L || c == Cfg::G4L;
 }
 
 const char *linear_config_name(const LinearArgs &a) {
@@ -1696,6 +1696,7 @@ hipError_t launch_linear(LinearArgs a, hipStream_t s) {
         case Cfg::G4K: return run_gemv<4, 16, 0, false, 2>(a, s);
         case Cfg::G1L: return run_gemv<1, 12, 0, false, 6>(a, s);
         case Cfg::G2L: return run_gemv<2, 12, 0, false, 6>(a, s);
+        case Cfg::G4L: return run_gemv<4, 12, 0, false, 6>(a, s);
         case Cfg::M1Long: return run_skinny<1, 1, 16, 2, 0>(a, s);
         case Cfg::M2Long: return run_skinny<2, 1, 16, 2, 0>(a, s);
         case Cfg::M4Long: return run_skinny<4, 1, 16, 2, 0>(a, s);
@@ -1724,6 +1725,8 @@ GemvCfg gemv_glu_cfg(Cfg c) { return gemv_cfg(c); }
 
 const char *linear_glu_config_name(int64_t M, int64_t K) {
     const Cfg c = pick_mk(M, K);
+    if (c == Cfg::G4L)
+        return skinny_name(M, K, 4, "skinny_kernel<4, 1, 8, 3, true, 0, true>", "skinny_kernel<4, 1, 8, 3, false, 0, true>");
     if (is_gemv(c)) {
         const GemvCfg g = gemv_glu_cfg(c);
         return gemv_name(g.mrows, g.wk, static_cast<int>((round_up(K, kTileK) / kTileK + g.wk - 1) / g.wk), g.wpe, true);
@@ -1751,6 +1754,7 @@ hipError_t launch_linear_glu(LinearArgs a, hipStream_t s) {
         case Cfg::G4K: return run_gemv<4, 16, 0, true, 2>(a, s);
         case Cfg::G1L: return run_gemv<1, 12, 0, true, 6>(a, s);
         case Cfg::G2L: return run_gemv<2, 12, 0, true, 6>(a, s);
+        case Cfg::G4L: return run_skinny<4, 1, 8, 3, 0, true>(a, s);   // 13.6 against 12.8 us as a 12-slice gemv
         case Cfg::M1Long: return run_skinny<1, 1, 8, 3, 0, true>(a, s);
         case Cfg::M2Long: return run_skinny<2, 1, 8, 3, 0, true>(a, s);
         case Cfg::M4Long: return run_skinny<4, 1, 8, 3, 0, true>(a, s);

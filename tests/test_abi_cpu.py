@@ -146,7 +146,11 @@ def test_linear_kernel_names(L):
     assert kn(1, 9216, arr(3072), 1) == b"gemv_kernel<1, 12, 6, 0, false>"   # long K: 12 K-slices
     assert kn(2, 5120, arr(3072), 1) == b"gemv_kernel<2, 12, 4, 0, false>"
     assert kn(1, 9248, arr(3072), 1) == b"skinny_kernel<1, 1, 16, 2, true, 0, false>"   # past 12 x 6 stages
-    assert kn(3, 9216, arr(3072), 1) == b"skinny_kernel<4, 1, 16, 2, true, 0, false>"
+    assert kn(3, 9216, arr(3072), 1) == b"gemv_kernel<4, 12, 6, 0, false>"
+    assert kn(4, 5120, arr(3072), 1) == b"gemv_kernel<4, 12, 4, 0, false>"
+    assert kn(4, 9248, arr(3072), 1) == b"skinny_kernel<4, 1, 16, 2, true, 0, false>"
+    assert L.q4_0_linear_swiglu_kernel(4, 9216) == b"skinny_kernel<4, 1, 8, 3, true, 0, true>"   # gated: K-split
+    assert L.q4_0_linear_swiglu_kernel(3, 4096) == b"gemv_kernel<4, 16, 2, 0, true>"
     assert L.q4_0_linear_swiglu_kernel(1, 9216) == b"gemv_kernel<1, 12, 6, 0, true>"
     assert L.q4_0_linear_swiglu_kernel(2, 9248) == b"skinny_kernel<2, 1, 8, 3, true, 0, true>"
     assert kn(2, 3072, arr(9216, 9216), 2) == b"gemv_kernel<2, 8, 3, 0, false>"

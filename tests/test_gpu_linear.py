@@ -38,13 +38,13 @@ def test_linear_parity_grid(m, n, k):
     _run_and_check(w, x, f"M={m} N={n} K={k}")
 
 
-# one and two rows on long rows: 12 K-slices of up to 6 stages (K 4097-9216;
+# up to four rows on long rows: 12 K-slices of up to 6 stages (K 4097-9216;
 # where 12 does not divide the super-tiles some stages lie past K, and a last
-# super-tile may be partial), the K-split kernel beyond 9216 and at 3-4 rows
+# super-tile may be partial), the K-split kernel beyond 9216
 LONG_NKS = [(40, 4128), (48, 5152), (24, 9184), (72, 9216), (16, 9248)]
 
 
-@pytest.mark.parametrize("m", [1, 2, 3])
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
 @pytest.mark.parametrize("n,k", LONG_NKS)
 def test_linear_long_rows(m, n, k):
     w = inputs.weights_f32((n, k), seed=23, tags=(n, k))

@@ -40,11 +40,12 @@ def test_swiglu_parity_grid(m, n, k):
     assert_within_bound(h, O.swiglu(x, gb, ub, n, k), O.swiglu_bound(x, gb, ub, n, k), f"swiglu M={m} N={n} K={k}")
 
 
-@pytest.mark.parametrize("m", [1, 2])
+@pytest.mark.parametrize("m", [1, 2, 4])
 @pytest.mark.parametrize("n,k", [(40, 5152), (24, 9184), (16, 9248)])
 def test_swiglu_long_rows(m, n, k):
-    """One and two rows on long rows: the gated 12-K-slice launch (dead and
-    partial stages) and the gated K-split kernel beyond K = 9216."""
+    """Up to four rows on long rows: the gated 12-K-slice launch at one and two
+    rows (dead and partial stages), the gated K-split kernel at four rows and
+    beyond K = 9216."""
     test_swiglu_parity_grid(m, n, k)
 
 
