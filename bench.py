@@ -15,7 +15,10 @@ Printed (one JSON line):
   roofline     the dominant kernel (the M=1 decode kernel) against 8 TB/s:
                algorithmic bytes of its launches / their summed kernel-own
                durations, taken with events armed on each launch of the timed
-               steps (q4_0_time_next_launch; an eager pass over the same K steps)
+               steps (q4_0_time_next_launch; an eager pass over the same K steps,
+               the launches held back until a whole step is queued so that they
+               run back to back as in the graph; with --isolated also the same
+               launches one at a time on an idle GPU, per_op_isolated_p10_p50_p90_us)
   workloads    one record per workload (1 the lone GEMV, 2 the decode step at
                M=1 and 2, 3 the LM head at M=1 and 32, 4 the M=2048 prefill,
                5 the audio linears): algorithmic bytes and flops, kernel-time
@@ -80,6 +83,8 @@ def parse_args():
     p.add_argument("--no-others", action="store_true",
                    help="skip the single GEMV and the audio linears (M = 1505, 6020)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
+    p.add_argument("--isolated", action="store_true",
+                   help="also time the decode launches one at a time on an idle GPU")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 256 MiB device copy (reference kernel for PMC byte counters)")
     return p.parse_args()
@@ -206,17 +211,39 @@ def pctl_us(times):
     return [round(float(np.percentile(times, q)) * 1e6, 2) for q in (10, 50, 90)]
 
 
-def time_kernels(runner, steps, dev):
+def _spin_ms_per_cycle(dev):
+    """Milliseconds per cycle of torch's spin kernel on this device."""
+    import torch
+
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream(dev)
+    a.record(stream)
+    torch.cuda._sleep(2_000_000)
+    b.record(stream)
+    b.synchronize()
+    return a.elapsed_time(b) / 2_000_000
+
+
+def time_kernels(runner, steps, dev, back_to_back=True):
     """Kernel-own durations of every launch over `steps` eager steps: each
-    launch is armed with an event pair that its kernel records at start/end."""
+    launch is armed with an event pair that its kernel records at start/end.
+
+    back_to_back (the default): the launches run one after another on a busy
+    GPU, as inside the timed graph.  Per step a spin kernel holds the stream
+    while the host enqueues the whole step; its length is checked per step
+    against the host's enqueue time (`runner.held` counts the timed steps
+    whose launches were all queued before the hold ended).  Otherwise
+    each launch follows the host's own launch overhead on an idle GPU
+    (isolated launches)."""
     import torch
 
     import q4_weight_only_amd as q4
 
     n = len(runner.items)
-    pairs = []
     stream = torch.cuda.current_stream(dev)
-    for _ in range(steps):
+
+    def enqueue_step(pairs):
         for i in range(n):
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
@@ -225,7 +252,40 @@ def time_kernels(runner, steps, dev):
             q4.time_next_launch(a, b)
             runner.launch(i)
             pairs.append((i, a, b))
+
+    pairs = []
+    held, cycles = 0, 0
+    if back_to_back:
+        t0 = time.perf_counter()
+        enqueue_step([])                   # untimed: the host's enqueue time of a step
+        cycles = int((2.0 * (time.perf_counter() - t0) * 1e3 + 2.0) / _spin_ms_per_cycle(dev))
+        torch.cuda.synchronize(dev)
+    # back to back: two untimed held steps first, which size the hold from the
+    # enqueue and hold times they measure (the spin's rate follows the clock)
+    warm = 2 if back_to_back else 0
+    for it in range(warm + steps):
+        if back_to_back:
+            h0 = torch.cuda.Event(enable_timing=True)
+            h1 = torch.cuda.Event(enable_timing=True)
+            t_hold = time.perf_counter()
+            h0.record(stream)
+            torch.cuda._sleep(cycles)
+            h1.record(stream)
+            step_pairs = []
+            enqueue_step(step_pairs)
+            enqueue_ms = (time.perf_counter() - t_hold) * 1e3
+            h1.synchronize()
+            hold = h0.elapsed_time(h1)
+            if it >= warm:
+                held += enqueue_ms < hold
+                pairs.extend(step_pairs)
+            need = 2.0 * enqueue_ms + 2.0
+            if hold < need:
+                cycles = int(cycles * need / hold)
+        else:
+            enqueue_step(pairs)
     torch.cuda.synchronize(dev)
+    runner.held = (held, steps) if back_to_back else None
     per_item = [[] for _ in range(n)]
     for i, a, b in pairs:
         per_item[i].append(a.elapsed_time(b) / 1e3)
@@ -667,7 +727,17 @@ def main():
         "per_op_GBs": {op: round(b / t / 1e9, 1) for op, (b, t, c) in per_op.items()},
         "per_op_avg_us": {op: round(t / c * 1e6, 2) for op, (b, t, c) in per_op.items()},
         "per_op_p10_p50_p90_us": {op: pctl_us(v) for op, v in per_op_times.items()},
+        "timing": "kernel-own (events armed on each launch), launches back to back as in the graph",
+        "steps_held": list(runner.held),
+        "step_kernel_sum_us": round(sum(sum(d) for d in durations) / args.steps * 1e6, 1),
     }
+    if args.isolated:
+        # the same launches one at a time on an otherwise idle GPU (host overhead between them)
+        iso = time_kernels(runner, args.steps, dev, back_to_back=False)
+        iso_op = collections.OrderedDict()
+        for (spec, *_), d in zip(runner.items, iso):
+            iso_op.setdefault(spec.name.split(".", 1)[1], []).extend(d)
+        roofline["per_op_isolated_p10_p50_p90_us"] = {op: pctl_us(v) for op, v in iso_op.items()}
     log(f"dominant decode kernel {dominant}: {achieved:.1f} GB/s over {launches} launches; per op {roofline['per_op_GBs']}")
 
     out = {
@@ -778,6 +848,8 @@ def main():
                 "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s",
                 "frac": round(pach / BF16_PEAK_TFLOPS, 4),
+                "timing": "kernel-own (events armed on each launch), launches back to back as in the graph",
+                "steps_held": list(prunner.held),
             },
             "per_op": {spec.name.split(".", 1)[1]: {
                 "kernel": name, "TFLOPs": round(flops(spec, 2048) * len(d) / sum(d) / 1e12, 2),
