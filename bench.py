@@ -211,31 +211,63 @@ def pctl_us(times):
     return [round(float(np.percentile(times, q)) * 1e6, 2) for q in (10, 50, 90)]
 
 
-def _spin_ms_per_cycle(dev):
-    """Milliseconds per cycle of torch's spin kernel on this device."""
-    import torch
+class Hold:
+    """Runs host-enqueued launches back to back on a busy GPU: a spin kernel
+    holds the stream while the host enqueues a batch of launches, so the
+    launches run one after another as inside a graph instead of one at a
+    time after the host's own launch overhead.  The spin's length (its rate
+    follows the clock) is raised whenever a batch's enqueue time comes within
+    half of it; `held` counts the counted batches that were queued in full
+    before the hold ended."""
 
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    stream = torch.cuda.current_stream(dev)
-    a.record(stream)
-    torch.cuda._sleep(2_000_000)
-    b.record(stream)
-    b.synchronize()
-    return a.elapsed_time(b) / 2_000_000
+    def __init__(self, dev, enqueue, warm=2):
+        import torch
+
+        self.stream = torch.cuda.current_stream(dev)
+        self.held = self.batches = 0
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        torch.cuda._sleep(2_000_000)
+        b.record(self.stream)
+        b.synchronize()
+        t0 = time.perf_counter()
+        enqueue()                          # untimed: the host's enqueue time of a batch
+        self.cycles = int((2.0 * (time.perf_counter() - t0) * 1e3 + 2.0) / (a.elapsed_time(b) / 2_000_000))
+        torch.cuda.synchronize(dev)
+        for _ in range(warm):              # untimed held batches size the hold
+            self.run(enqueue, count=False)
+
+    def run(self, enqueue, count=True):
+        import torch
+
+        h0 = torch.cuda.Event(enable_timing=True)
+        h1 = torch.cuda.Event(enable_timing=True)
+        t_hold = time.perf_counter()
+        h0.record(self.stream)
+        torch.cuda._sleep(self.cycles)
+        h1.record(self.stream)
+        enqueue()
+        enqueue_ms = (time.perf_counter() - t_hold) * 1e3
+        h1.synchronize()
+        hold = h0.elapsed_time(h1)
+        if count:
+            self.held += enqueue_ms < hold
+            self.batches += 1
+        need = 2.0 * enqueue_ms + 2.0
+        if hold < need:
+            self.cycles = int(self.cycles * need / hold)
 
 
 def time_kernels(runner, steps, dev, back_to_back=True):
     """Kernel-own durations of every launch over `steps` eager steps: each
     launch is armed with an event pair that its kernel records at start/end.
 
-    back_to_back (the default): the launches run one after another on a busy
-    GPU, as inside the timed graph.  Per step a spin kernel holds the stream
-    while the host enqueues the whole step; its length is checked per step
-    against the host's enqueue time (`runner.held` counts the timed steps
-    whose launches were all queued before the hold ended).  Otherwise
-    each launch follows the host's own launch overhead on an idle GPU
-    (isolated launches)."""
+    back_to_back (the default): each step's launches are enqueued under a
+    Hold and run one after another on a busy GPU, as inside the timed graph
+    (`runner.held`: timed steps queued in full before the hold ended).
+    Otherwise each launch follows the host's own launch overhead on an idle
+    GPU (isolated launches)."""
     import torch
 
     import q4_weight_only_amd as q4
@@ -254,38 +286,16 @@ def time_kernels(runner, steps, dev, back_to_back=True):
             pairs.append((i, a, b))
 
     pairs = []
-    held, cycles = 0, 0
     if back_to_back:
-        t0 = time.perf_counter()
-        enqueue_step([])                   # untimed: the host's enqueue time of a step
-        cycles = int((2.0 * (time.perf_counter() - t0) * 1e3 + 2.0) / _spin_ms_per_cycle(dev))
-        torch.cuda.synchronize(dev)
-    # back to back: two untimed held steps first, which size the hold from the
-    # enqueue and hold times they measure (the spin's rate follows the clock)
-    warm = 2 if back_to_back else 0
-    for it in range(warm + steps):
-        if back_to_back:
-            h0 = torch.cuda.Event(enable_timing=True)
-            h1 = torch.cuda.Event(enable_timing=True)
-            t_hold = time.perf_counter()
-            h0.record(stream)
-            torch.cuda._sleep(cycles)
-            h1.record(stream)
-            step_pairs = []
-            enqueue_step(step_pairs)
-            enqueue_ms = (time.perf_counter() - t_hold) * 1e3
-            h1.synchronize()
-            hold = h0.elapsed_time(h1)
-            if it >= warm:
-                held += enqueue_ms < hold
-                pairs.extend(step_pairs)
-            need = 2.0 * enqueue_ms + 2.0
-            if hold < need:
-                cycles = int(cycles * need / hold)
-        else:
+        hold = Hold(dev, lambda: enqueue_step([]))
+        for _ in range(steps):
+            hold.run(lambda: enqueue_step(pairs))
+        runner.held = (hold.held, hold.batches)
+    else:
+        for _ in range(steps):
             enqueue_step(pairs)
+        runner.held = None
     torch.cuda.synchronize(dev)
-    runner.held = (held, steps) if back_to_back else None
     per_item = [[] for _ in range(n)]
     for i, a, b in pairs:
         per_item[i].append(a.elapsed_time(b) / 1e3)
@@ -301,8 +311,9 @@ def time_swiglu(prepared, ms, reps, dev):
     Two more kinds are timed by events recorded on the stream around the
     calls (launch gaps included): the fused launch, and the unfused launch
     followed by torch's silu(g) * u into h (the unfused step in full).
-    Each kind's time is the median over its launches; two untimed passes
-    over every kind come first (the GPU has been idle through the host-side
+    Each kind's pass over the pairs runs back to back under a Hold, as the
+    step's launches do.  Each kind's time is the median over its launches;
+    two untimed passes over every kind come first (the GPU has been idle through the host-side
     oracle timing before this, and a single pass left the first kind's
     launches up to a third slower in some runs)."""
     import numpy as np
@@ -323,31 +334,37 @@ def time_swiglu(prepared, ms, reps, dev):
         ys = [torch.empty((m, n), dtype=torch.float32, device=dev) for _ in range(2)]
         kinds = ("fused", "fused_bf16", "unfused", "fused_stream", "unfused_silu_stream")
         pairs = {kind: [] for kind in kinds}
+
+        def batch(kind, keep):
+            for _, pws in gate_up:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                if kind.endswith("_stream"):
+                    a.record(stream)
+                    if kind == "fused_stream":
+                        q4.linear_swiglu(x, pws[0], pws[1], h)
+                    else:
+                        q4.linear_multi(x, pws, ys)
+                        torch.mul(torch.nn.functional.silu(ys[0]), ys[1], out=h)
+                    b.record(stream)
+                else:
+                    a.record(stream)
+                    b.record(stream)
+                    q4.time_next_launch(a, b)
+                    if kind == "fused":
+                        q4.linear_swiglu(x, pws[0], pws[1], h)
+                    elif kind == "fused_bf16":
+                        q4.linear_swiglu(x, pws[0], pws[1], h16, dtype=torch.bfloat16)
+                    else:
+                        q4.linear_multi(x, pws, ys)
+                if keep:
+                    pairs[kind].append((a, b))
+
+        # each kind's pass over the 26 pairs runs back to back under a hold
+        hold = Hold(dev, lambda: batch("fused", False), warm=0)
         for r in range(reps + 2):
             for kind in kinds:
-                for _, pws in gate_up:
-                    a = torch.cuda.Event(enable_timing=True)
-                    b = torch.cuda.Event(enable_timing=True)
-                    if kind.endswith("_stream"):
-                        a.record(stream)
-                        if kind == "fused_stream":
-                            q4.linear_swiglu(x, pws[0], pws[1], h)
-                        else:
-                            q4.linear_multi(x, pws, ys)
-                            torch.mul(torch.nn.functional.silu(ys[0]), ys[1], out=h)
-                        b.record(stream)
-                    else:
-                        a.record(stream)
-                        b.record(stream)
-                        q4.time_next_launch(a, b)
-                        if kind == "fused":
-                            q4.linear_swiglu(x, pws[0], pws[1], h)
-                        elif kind == "fused_bf16":
-                            q4.linear_swiglu(x, pws[0], pws[1], h16, dtype=torch.bfloat16)
-                        else:
-                            q4.linear_multi(x, pws, ys)
-                    if r > 1:              # the first two passes warm up
-                        pairs[kind].append((a, b))
+                hold.run(lambda: batch(kind, r > 1), count=r > 1)   # the first two passes warm up
         torch.cuda.synchronize(dev)
         t = {kind: float(np.median([a.elapsed_time(b) / 1e3 for a, b in v])) for kind, v in pairs.items()}
         wbytes = spec0.weight_bytes()
@@ -366,6 +383,7 @@ def time_swiglu(prepared, ms, reps, dev):
             "fused_TFLOPs": round(fl / t["fused"] / 1e12, 2),
             "unfused_TFLOPs": round(fl / t["unfused"] / 1e12, 2),
             "launches": len(pairs["fused"]),
+            "passes_held": [hold.held, hold.batches],
         }
     return out
 
