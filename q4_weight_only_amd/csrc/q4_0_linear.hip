@@ -972,8 +972,8 @@ struct Gemm3Cfg {
 
 // GLU: gate / up as in skinny_kernel: the first WN / 2 waves of a workgroup
 // row run gate rows, the last WN / 2 the same rows of up, each exactly as a
-// plain launch would; the up waves hand their results to the gate waves
-// through LDS for the silu(gate) * up epilogue.
+// plain launch would; each gate wave and its up wave trade half of their
+// results through LDS and form silu(gate) * up for half the m-tiles each.
 //
 // ASYM: the asymmetric layout (w = q d + m).  The codes are decoded as q and
 // each block's product D is rescaled by d as in the symmetric kernel; the
@@ -1237,20 +1237,21 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
     }
     if constexpr (ASYM) offset_term((KT - 1) >> 1, (KT & 1) != 0);   // the last window (one step if KT is odd)
 
-    // gated: the up waves leave their results in LDS (the x buffers are free
-    // once the last step's barrier has passed) for the matching gate wave
+    // gated: a gate wave and its up wave split the epilogue. The gate wave
+    // leaves g of its last MT / 2 m-tiles in LDS, the up wave u of its first
+    // MT / 2 (the x buffers are free once the last step's barrier has passed);
+    // each then forms silu(g) * u for its own half of the m-tiles.
+    static_assert(!GLU || MT % 2 == 0, "the gated epilogue splits the m-tiles in halves");
     float *xch = reinterpret_cast<float *>(&lds_a[0][0]) + (wm * WNO + wno) * (MT * NT * 4 * 64);
     if constexpr (GLU) {
-        if (up_wave) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
+            if ((mt < MT / 2) == up_wave)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) xch[((mt * NT + nt) * 4 + r) * 64 + lane] = acc[mt][nt][r];
-        }
         __syncthreads();
-        if (up_wave) return;
     }
 
 #pragma unroll
@@ -1259,18 +1260,22 @@ void gemm3_kernel(const LinearArgs a, const int mtiles, const int ntiles) {
         const int n = rt * 16 + nl;
         if (rt >= sg.RT || n >= sg.N) continue;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+            if (GLU && (mt < MT / 2) == up_wave) continue;   // the other wave of the pair stores these
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + (wm * MT + mt) * 16 + 4 * g + r;
                 if (m >= a.M) continue;
                 const float v = ASYM ? acc[mt][nt][r] : acc[mt][nt][r] * 16.0f;
-                if constexpr (GLU)
+                if constexpr (GLU) {
+                    const float other = xch[((mt * NT + nt) * 4 + r) * 64 + lane] * 16.0f;
                     store_out(a, sg, static_cast<int64_t>(m) * sg.N + n,
-                              silu_f32(v) * (xch[((mt * NT + nt) * 4 + r) * 64 + lane] * 16.0f));
-                else
+                              up_wave ? silu_f32(other) * v : silu_f32(v) * other);
+                } else {
                     sg.y[static_cast<int64_t>(m) * sg.N + n] = v;
+                }
             }
+        }
     }
 }
 
