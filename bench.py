@@ -7,7 +7,8 @@ A step is one decode step of the 26-layer decoder's linears at M=1 (fused
 QKV 3072->4096+1024+1024, O 4096->3072, fused gate/up 3072->2x9216,
 down 9216->3072 per layer: 104 launches, 1.70 GB of distinct Q4_0 weights),
 with every input already resident in HBM.  The step is captured once in a HIP
-graph and replayed; K replays are timed with HIP events on the replay stream.
+graph and replayed; K replays are timed between two HIP events on the replay
+stream (K more, with an event after each, give the single-step spread).
 
 Printed (one JSON line):
   value        eff. HBM GB/s of the whole step: algorithmic bytes per step
@@ -178,8 +179,9 @@ class Runner:
 
 
 def time_graph(runner, steps, warmup, dev):
-    """Capture one step in a HIP graph; time `steps` replays with events (one
-    between every two replays, so each step's time is kept too)."""
+    """Capture one step in a HIP graph; time `steps` replays between two
+    events, then `steps` more with an event after each replay (each step's
+    time, kept in runner.step_times)."""
     import torch
 
     stream = torch.cuda.Stream(dev)
@@ -194,15 +196,25 @@ def time_graph(runner, steps, warmup, dev):
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             graph.replay()
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        # the timed region: K replays between two events and nothing else
+        # (an event between every two replays costs about 4 us per step here)
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize(dev)
+        start.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        stop.record(stream)
+        torch.cuda.synchronize(dev)
+        # then K more replays with an event after each, for the spread of single steps
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         marks[0].record(stream)
         for i in range(steps):
             graph.replay()
             marks[i + 1].record(stream)
     marks[-1].synchronize()
     runner.step_times = [marks[i].elapsed_time(marks[i + 1]) / 1e3 for i in range(steps)]
-    return marks[0].elapsed_time(marks[-1]) / 1e3, graph
+    return start.elapsed_time(stop) / 1e3, graph
 
 
 def pctl_us(times):
